@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV-cache hot path on one MI355X.
+
+One step = the whole hot path over one batch: host bookkeeping (slot and
+copy-on-write reservation in the block manager, block-table export), the
+host-to-device copy of the tables, the copy-on-write block copy (when any),
+the cache append of one token per sequence, and split-context decode
+attention with its log-sum-exp merge.  Consecutive steps are real decode
+steps: every sequence grows by one token per step, new blocks are taken at
+block boundaries.
+
+Default workload: the Llama-3-70B-shaped decode layer at 32k context
+(16 sequences x 32768 tokens, 64 query / 8 kv heads, head_dim 128, bf16,
+block 16, 40k-block pool, blocks scattered by a seeded permutation).  All
+inputs are synthetic and resident in HBM before the timed region.
+
+Prints one JSON line: ``value`` = whole-job KV throughput (algorithmic K/V
+bytes of valid tokens / wall time per step), plus tokens/s, the roofline of
+the decode call measured with HIP events on its stream, and the CPU oracle
+timed on the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attention KV GB/s (% of HBM peak) and tokens/s, 70B-shaped layer @32k"
+HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_230_amd", "csrc", "pagedkv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c3_traffic.json")
+
+
+# ------------------------------------------------------------- accounting
+def decode_algorithmic_bytes(lens, num_q_heads, num_kv_heads, head_dim, block_size, elem_bytes):
+    """Bytes a decode call must move at minimum: K/V of valid tokens (each
+    read once, shared by the G query heads of its kv head), q and out, the
+    used block-table entries and the lengths."""
+    kv = sum(int(L) for L in lens) * num_kv_heads * head_dim * 2 * elem_bytes
+    qo = 2 * len(lens) * num_q_heads * head_dim * elem_bytes
+    tables = 4 * sum(-(-int(L) // block_size) for L in lens)
+    return kv + qo + tables + 4 * len(lens)
+
+
+def decode_kv_bytes(lens, num_kv_heads, head_dim, elem_bytes):
+    return sum(int(L) for L in lens) * num_kv_heads * head_dim * 2 * elem_bytes
+
+
+def decode_flops(lens, num_q_heads, head_dim):
+    return sum(4 * num_q_heads * head_dim * int(L) for L in lens)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per decode call from committed counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_decode_call")
+
+
+# ----------------------------------------------------------------- CPU leg
+def cpu_baseline(workload_name, num_seqs):
+    """The oracle (unchanged) timed on one decode step of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.runner import OracleRun
+    from workloads import Workload
+
+    over = {} if num_seqs is None else dict(num_seqs=num_seqs)
+    w = Workload(workload_name, overrides=over)
+    run = OracleRun(w)  # untimed: materialise the pools for the sample
+    q = w.q(0)
+    t0 = time.perf_counter()
+    run.step(0)
+    ref = run.attention(q)
+    dt = time.perf_counter() - t0
+    _, lens = run.tables()
+    c = w.config
+    kv = decode_kv_bytes(lens, c.num_kv_heads, c.head_dim, c.elem_bytes)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    assert np.isfinite(ref).all()
+    return {
+        "value": kv / dt / 1e9,
+        "unit": "GB/s",
+        "tokens_per_s": w.num_seqs / dt,
+        "seconds": dt,
+        "cores": int(threads),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"one full decode step (bookkeeping, append, fp64 gather+attention) of {w.num_seqs} "
+                  f"sequences of {workload_name}, lengths {int(min(lens))}..{int(max(lens))}",
+    }
+
+
+# ----------------------------------------------------------------- GPU leg
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3_70b_32k_bf16")
+    ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences in the oracle sample (default: all)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU sharding of this path is a design note, not a measured configuration.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_230_amd as pkv
+    from workloads import Workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = Workload(args.workload)
+    c = w.config
+    S = w.num_seqs
+    nsteps = args.warmup + args.steps
+    print(f"# setup {w.name}: {S} sequences, pool {w.num_blocks} blocks", file=sys.stderr, flush=True)
+    t_setup = time.perf_counter()
+    cache = pkv.PagedKVCache(w.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.torch_dtype, dev,
+                             w.free_order)
+    for op in w.setup_ops:
+        cache.apply(op, w.kv)
+    torch.cuda.synchronize()
+    print(f"# setup done in {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    # Per-step inputs, resident on the GPU before timing.
+    step_k, step_v, step_q = [], [], []
+    for k in range(nsteps):
+        kn, vn = w.kv(("step", k))
+        step_k.append(kn.to(dev))
+        step_v.append(vn.to(dev))
+        step_q.append(w.q(k).to(dev))
+
+    bm = cache.bm
+    seqs = np.asarray(w.decode_seqs, np.int64)
+    bs = c.block_size
+    max_len_bound = int(max(bm.seq_len(int(s)) for s in seqs)) + nsteps
+    max_blocks = -(-max_len_bound // bs)
+    P = args.partition if args.partition else pkv.paged_attention_default_partition(
+        S, c.num_kv_heads, c.head_dim, bs, max_len_bound)
+    ws_bytes = pkv.paged_attention_workspace_bytes(S, c.num_q_heads, c.num_kv_heads, c.head_dim, bs, max_len_bound, P)
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty(S, c.num_q_heads, c.head_dim, dtype=c.torch_dtype, device=dev)
+    tables_d = torch.empty(S, max_blocks, dtype=torch.int32, device=dev)
+    lens_d = torch.empty(S, dtype=torch.int32, device=dev)
+    slots_d = torch.empty(S, dtype=torch.int32, device=dev)
+    pairs_d = torch.empty(S, 2, dtype=torch.int32, device=dev)
+    RING = 2
+    tables_h = [torch.empty(S, max_blocks, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
+    lens_h = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
+    slots_h = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
+    pairs_h = [torch.empty(S, 2, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
+    h2d_done = [torch.cuda.Event() for _ in range(RING)]
+    for e in h2d_done:
+        e.record()
+    ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
+    host_s = [0.0] * nsteps
+    seg = {"sync": 0.0, "bookkeeping": 0.0, "h2d": 0.0, "append": 0.0, "decode": 0.0}
+    step_lens = []
+    n_cow = 0
+
+    def step(k):
+        nonlocal n_cow
+        th = time.perf_counter()
+        r = k % RING
+        h2d_done[r].synchronize()  # the copies that last read ring slot r are done
+        ev_start[k].record()
+        t1 = time.perf_counter()
+        slots, pairs = bm.append_slots(seqs)
+        tnp, lnp = tables_h[r].numpy(), lens_h[r].numpy()
+        bm.block_tables(seqs, max_blocks, tnp, lnp)
+        slots_h[r].numpy()[:] = slots
+        npairs = pairs.shape[0]
+        if npairs:
+            pairs_h[r].numpy()[:npairs] = pairs
+            n_cow += npairs
+        step_lens.append(lnp.copy())
+        t2 = time.perf_counter()
+        tables_d.copy_(tables_h[r], non_blocking=True)
+        lens_d.copy_(lens_h[r], non_blocking=True)
+        slots_d.copy_(slots_h[r], non_blocking=True)
+        if npairs:
+            pairs_d[:npairs].copy_(pairs_h[r][:npairs], non_blocking=True)
+        h2d_done[r].record()
+        t3 = time.perf_counter()
+        if npairs:
+            pkv.paged_kv_copy_blocks(cache.k_cache, cache.v_cache, pairs_d[:npairs])
+        pkv.paged_kv_append(step_k[k], step_v[k], cache.k_cache, cache.v_cache, slots_d)
+        ev0[k].record()
+        t4 = time.perf_counter()
+        pkv.paged_attention_decode(out, step_q[k], cache.k_cache, cache.v_cache, tables_d, lens_d,
+                                   int(lnp.max()), partition_size=P, workspace=workspace)
+        ev1[k].record()
+        t5 = time.perf_counter()
+        host_s[k] = t5 - th
+        if k >= args.warmup:
+            for name, dt in (("sync", t1 - th), ("bookkeeping", t2 - t1), ("h2d", t3 - t2), ("append", t4 - t3),
+                             ("decode", t5 - t4)):
+                seg[name] += dt
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for k in range(args.warmup, nsteps):
+        step(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"# timed {args.steps} steps in {elapsed:.4f}s; host us/step by segment: "
+          + ", ".join(f"{k}={1e6 * v / args.steps:.1f}" for k, v in seg.items()), file=sys.stderr, flush=True)
+
+    timed = range(args.warmup, nsteps)
+    dec_ms = [ev0[k].elapsed_time(ev1[k]) for k in timed]
+    lens_t = [step_lens[k] for k in timed]
+    kv_bytes = [decode_kv_bytes(L, c.num_kv_heads, c.head_dim, c.elem_bytes) for L in lens_t]
+    alg_bytes = [decode_algorithmic_bytes(L, c.num_q_heads, c.num_kv_heads, c.head_dim, bs, c.elem_bytes)
+                 for L in lens_t]
+    flops = [decode_flops(L, c.num_q_heads, c.head_dim) for L in lens_t]
+    mean_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
+    achieved = (sum(alg_bytes) / len(alg_bytes)) / mean_dec_s
+    ms_per_step = elapsed / args.steps * 1e3
+    value = sum(kv_bytes) / elapsed / 1e9
+    traffic = load_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_seqs": S,
+            "context_len_first_step": int(lens_t[0].min()),
+            "num_q_heads": c.num_q_heads,
+            "num_kv_heads": c.num_kv_heads,
+            "head_dim": c.head_dim,
+            "block_size": bs,
+            "num_blocks": w.num_blocks,
+            "partition_size": P,
+        },
+        "tokens_per_s": round(S * args.steps / elapsed, 1),
+        "pct_hbm_peak_whole_step": round(100.0 * value * 1e9 / HBM_PEAK, 2),
+        "decode_call_us": round(mean_dec_s * 1e6, 2),
+        "decode_kv_gbps": round((sum(kv_bytes) / len(kv_bytes)) / mean_dec_s / 1e9, 2),
+        "decode_tflops": round((sum(flops) / len(flops)) / mean_dec_s / 1e12, 2),
+        "cow_pairs": n_cow,
+        "host_us_per_step": round(1e6 * sum(host_s[k] for k in timed) / args.steps, 1),
+        "gpu_step_us": round(1e3 * sum(ev_start[k].elapsed_time(ev1[k]) for k in timed) / args.steps, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attention_decode (partition kernel + log-sum-exp merge)",
+            "achieved": round(achieved / 1e9, 2),
+            "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_call": int(sum(alg_bytes) / len(alg_bytes)),
+        },
+        "cpu_baseline": None,
+    }
+    del cache, step_k, step_v, step_q, workspace
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("# cpu baseline: oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seqs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,234 @@
+/*
+ * pagedkv.h -- C ABI of the paged KV-cache decode library (gfx950 / MI355X).
+ *
+ * The library implements the data-parallel hot path of PagedAttention:
+ *   - a host block manager (free pool, reference counts, copy-on-write),
+ *   - the copy-on-write block copy and the cache append on the GPU,
+ *   - single-query decode attention that reads K/V through per-sequence
+ *     block tables, split over context partitions and merged by log-sum-exp.
+ *
+ * Sources (page title, section):
+ *   [gloss]  "PagedAttention" (ayinedjimi-consultants.fr glossary), Définition
+ *   [sheet]  "PagedAttention — Gestion mémoire pour LLM à long contexte"
+ *            (analyticslegends.ai), Pourquoi c'est important / Points clés /
+ *            Termes employés sur cette page
+ *   [pl]     "PagedAttention" (robocikowo.com), Jak działa / Komponenty /
+ *            Złożoność obliczeniowa
+ *   [aitalk] "PagedAttention et RadixAttention : parlons de KV Cache"
+ *            (aitalk.it), section "PagedAttention : la mémoire comme un
+ *            système d'exploitation", steps 1-4 and closing paragraph
+ *
+ * General conventions
+ *   - Every function returns an int32 status (PKV_OK = 0, negative on
+ *     error) unless stated; pkv_last_error() then describes the failure for
+ *     the calling thread.
+ *   - Device pointers are plain device addresses (e.g. from hipMalloc or a
+ *     framework tensor).  The caller owns every buffer, including the
+ *     decode workspace; the library never allocates device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Device entry points only enqueue work on it and return; ordering is
+ *     the stream's.  They validate sizes and pointers on the host before
+ *     launching; device-side indices (slots, block ids, lengths) are range
+ *     checked in the kernels so bad values never touch memory outside the
+ *     buffers (the affected results are then unspecified).
+ *   - Device entry points are re-entrant.  A block manager handle must be
+ *     used by one thread at a time.
+ *
+ * Pool format (both pools hold one layer; the caller allocates them):
+ *   x = 16 / sizeof(element)  (4 for fp32, 8 for bf16)
+ *   K pool: [num_blocks][num_kv_heads][head_dim / x][block_size][x]
+ *           token o of block b, kv head h, dimension i is element
+ *           [b][h][i / x][o][i % x]
+ *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]
+ *           element [b][h][i][o]
+ *   Slot s addresses token offset s % block_size of block s / block_size.
+ *   The pages fix fixed-size blocks of token slots, 16 or 32 per block, per
+ *   layer, placed anywhere in GPU memory ([gloss] Définition; [sheet] Points
+ *   clés; [pl] Jak działa; [aitalk] step 1); the byte layout inside a block is
+ *   this library's choice: every (block, kv head) tile is contiguous and the
+ *   layout gives whole-wavefront contiguous 16-byte loads in the decode
+ *   kernel's matrix-core operand order.
+ *
+ * Supported shapes: dtype PKV_F32 or PKV_BF16; head_dim 64 or 128;
+ * block_size 16 or 32; num_q_heads a multiple of num_kv_heads with group
+ * size G = num_q_heads / num_kv_heads <= 8 (bf16) or <= 16 (fp32).
+ * Query head h uses kv head h / G.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_ERR_INVALID_ARG (-1)   /* bad size, pointer, alignment or id     */
+#define PKV_ERR_OUT_OF_BLOCKS (-2) /* free pool cannot satisfy the request   */
+#define PKV_ERR_UNKNOWN_SEQ (-3)   /* sequence id not registered             */
+#define PKV_ERR_DEVICE (-4)        /* a HIP call or kernel launch failed     */
+#define PKV_ERR_UNSUPPORTED (-5)   /* dtype/head_dim/block_size/G not built  */
+#define PKV_ERR_CAPACITY (-6)      /* caller's output buffer too small       */
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Message for the last failing call on this thread ("" if none).  The
+ * string is owned by the library and valid until the thread's next call. */
+const char* pkv_last_error(void);
+
+/* Library interface version (major * 100 + minor). */
+int32_t pkv_version(void);
+
+/* ------------------------------------------------------------------ */
+/* Cache append ([aitalk] step 3: the cache grows one slot at a time; a  */
+/* token is written into the slot the block manager reserved for it).    */
+/*                                                                        */
+/* k_new, v_new : device, [num_tokens][num_kv_heads][head_dim], dtype dt, */
+/*                16-byte aligned rows                                    */
+/* k_cache, v_cache : device pools in the format above, num_blocks blocks */
+/* slot_mapping : device int32 [num_tokens]; slot < 0 skips the token;    */
+/*                slots must be distinct (duplicates race)                */
+/* Writes K/V of each token into its slot; every other byte is untouched. */
+/* num_tokens == 0 is a no-op.                                            */
+int32_t paged_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks, pkv_dtype dt,
+                        void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Copy-on-write block copy ([pl] Komponenty: reference counting with    */
+/* lazy duplication; [aitalk] step 4: a shared block is copied only when */
+/* a sequence diverges from the others).                                 */
+/*                                                                        */
+/* src_dst : device int32 [num_pairs][2] = (source block, destination     */
+/*           block); whole blocks (all kv heads, all slots) of both pools */
+/*           are copied.  Pairs run concurrently: no destination may be a */
+/*           source or destination of another pair (the block manager's   */
+/*           pairs satisfy this).  num_pairs == 0 is a no-op.             */
+int32_t paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst, int32_t num_pairs,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             pkv_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Decode attention ([pl] Jak działa and Komponenty: an attention kernel  */
+/* that reads a non-contiguous cache through the block table; [aitalk]   */
+/* step 2 and closing paragraph: the sequence appears contiguous and the */
+/* attention result is unchanged by paging).                             */
+/*                                                                        */
+/* For each sequence s (context length L = context_lens[s], the number   */
+/* of cached tokens to attend to, including one appended this step) and  */
+/* query head h (kv head g = h / G):                                      */
+/*   out[s][h] = sum_t softmax_t(scale * <q[s][h], K_t[g]>) V_t[g],       */
+/* t over the first L slots named by block_tables[s].  L == 0 gives a    */
+/* zero row.  Scores, softmax and the weighted sum are computed in fp32;  */
+/* bf16 outputs are rounded to nearest-even.                             */
+/*                                                                        */
+/* out, q        : device, [num_seqs][num_q_heads][head_dim], dtype dt    */
+/* k_cache, v_cache : device pools, num_blocks blocks                     */
+/* block_tables  : device int32 [num_seqs][max_blocks_per_seq]; entries   */
+/*                 past ceil(L / block_size) are not read                 */
+/* context_lens  : device int32 [num_seqs], each in [0, max_context_len]  */
+/* max_context_len : host upper bound on context_lens, <=                 */
+/*                 max_blocks_per_seq * block_size                        */
+/* scale         : logit scale (usually 1/sqrt(head_dim))                 */
+/* partition_size: tokens per context partition (a multiple of            */
+/*                 block_size) -- each (sequence, kv head, partition) is  */
+/*                 one workgroup, partitions are merged by log-sum-exp;   */
+/*                 0 picks paged_attention_default_partition()            */
+/* workspace     : device scratch for partition partials, at least        */
+/*                 paged_attention_workspace_bytes(...) bytes, 256-byte   */
+/*                 aligned; may be NULL when that size is 0.  Its content */
+/*                 is overwritten; calls sharing a workspace must be      */
+/*                 ordered on one stream.                                 */
+int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                               float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                               pkv_dtype dt, void* stream);
+
+/* The partition size that partition_size == 0 selects (a multiple of     */
+/* block_size), or a negative status for invalid arguments.               */
+int32_t paged_attention_default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_context_len);
+
+/* Workspace bytes paged_attention_decode needs for these arguments (0    */
+/* when every sequence fits one partition).  Returns 0 and sets the last  */
+/* error for invalid arguments (check pkv_last_error() if 0 is            */
+/* unexpected).                                                            */
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                       int32_t partition_size);
+
+/* ------------------------------------------------------------------ */
+/* Host block manager ([pl] Komponenty: block table, block manager with a */
+/* free pool, reference counting + copy-on-write; [aitalk] steps 1-4;     */
+/* [sheet] Pourquoi c'est important: pages allocated on demand and freed  */
+/* one by one; [gloss] Définition: unused blocks recycled at once).      */
+/*                                                                        */
+/* Policy (deterministic; the pages leave it open):                       */
+/*   - free pool = stack; initial_free_order[0] is handed out first;      */
+/*     released blocks go on top and are reused first; a released         */
+/*     sequence returns its blocks in logical order 0..n-1.               */
+/*   - appending a token at length L: if L % block_size == 0 a fresh      */
+/*     block is appended to the table; otherwise, if the block holding    */
+/*     slot L is shared (refcount > 1), a fresh block replaces it and the */
+/*     pair (old, fresh) is reported for paged_kv_copy_blocks; the slot   */
+/*     is table[L / bs] * bs + L % bs.  Sequences are processed in call   */
+/*     order; the last holder of a shared block writes in place.          */
+/*   - every call is atomic: on error nothing changes.                    */
+/* All pointers here are host pointers.                                    */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* initial_free_order: num_blocks distinct ids (a permutation), or NULL   */
+/* for 0..num_blocks-1.  *out receives the handle.                        */
+int32_t pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order,
+                      pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* Register an empty sequence (L = 0).  Error if the id exists. */
+int32_t pkv_bm_add_seq(pkv_block_manager* bm, int64_t seq_id);
+
+/* Register `child` sharing the first ceil(num_tokens / bs) blocks of      */
+/* `parent` (refcount + 1 each), with L = num_tokens <= L(parent).         */
+int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child, int32_t num_tokens);
+
+/* Reserve slots for new tokens.                                           */
+/* seq_ids     : [n_seqs] distinct registered ids                          */
+/* num_tokens  : [n_seqs] tokens per sequence (>= 0), or NULL for 1 each   */
+/* slot_mapping_out : [slot_capacity]; receives the slots, sequence-major  */
+/* cow_pairs_out    : [cow_capacity][2]; receives (src, dst) block copies  */
+/*                    that must run before the tokens are written          */
+/* *n_slots_out, *n_cow_out : counts written (either may be NULL)          */
+int32_t pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs,
+                            const int32_t* num_tokens, int32_t* slot_mapping_out, int32_t slot_capacity,
+                            int32_t* n_slots_out, int32_t* cow_pairs_out, int32_t cow_capacity,
+                            int32_t* n_cow_out);
+
+/* Release a sequence: refcount - 1 on each block, blocks reaching 0 go   */
+/* back to the free pool.                                                  */
+int32_t pkv_bm_free_seq(pkv_block_manager* bm, int64_t seq_id);
+
+/* Export block tables and lengths.                                        */
+/* tables_out       : [n_seqs][max_blocks_per_seq], rows padded with -1    */
+/* context_lens_out : [n_seqs] (may be NULL)                               */
+/* PKV_ERR_CAPACITY if a table is wider than max_blocks_per_seq.           */
+int32_t pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs,
+                            int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out);
+
+/* Queries.  Negative status on a bad handle or id.                        */
+int32_t pkv_bm_num_free(const pkv_block_manager* bm);
+int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);
+int32_t pkv_bm_seq_len(const pkv_block_manager* bm, int64_t seq_id);
+int32_t pkv_bm_num_seqs(const pkv_block_manager* bm);
+/* Free pool, bottom to top (the next block handed out is last);          */
+/* capacity >= pkv_bm_num_free().                                          */
+int32_t pkv_bm_free_stack(const pkv_block_manager* bm, int32_t* out, int32_t capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -56,11 +56,11 @@ def dense_attention(q_row, k_seq, v_seq, scale):
     out = np.zeros((Hq, d), dtype=np.float64)
     if L == 0:
         return out
-    for h in range(Hq):
-        g = h // G
-        x = (k_seq[:, g, :] @ q_row[h]) * scale
-        p = np.exp(x - x.max())
-        out[h] = (p @ v_seq[:, g, :]) / p.sum()
+    for g in range(Hkv):
+        heads = slice(g * G, (g + 1) * G)  # query heads h with h // G == g
+        x = (k_seq[:, g, :] @ q_row[heads].T) * scale  # [L][G] logits
+        p = np.exp(x - x.max(axis=0))
+        out[heads] = (p.T @ v_seq[:, g, :]) / p.sum(axis=0)[:, None]
     return out
 
 

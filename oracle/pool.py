@@ -77,9 +77,10 @@ def append(k_pool, v_pool, k_new, v_new, slot_mapping):
         raise IndexError("slot outside the pool")
     b = slots // bs
     o = slots % bs
-    for t in range(len(slots)):
-        k_pool[b[t], :, :, o[t], :] = kn[t].reshape(H, nch, x)
-        v_pool[b[t], :, :, o[t]] = vn[t]
+    # Advanced indices on the block and slot axes: element t of the result
+    # is token t's [H][d/x][x] chunk grid (slots are distinct).
+    k_pool[b, :, :, o, :] = kn.reshape(len(slots), H, nch, x)
+    v_pool[b, :, :, o] = vn
 
 
 def copy_blocks(k_pool, v_pool, pairs):

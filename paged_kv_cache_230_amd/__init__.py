@@ -1,0 +1,19 @@
+"""MI355X-native paged KV-cache decode attention.
+
+Python binding of ``libpagedkv.so`` (C ABI: ``include/pagedkv.h``).  The
+functions below only marshal torch tensors into the library's entry points
+of the same names; the HIP kernels and the C++ block manager do the work.
+Importing fails if the library has not been built (no CPU fallback).
+"""
+from ._native import EXPORTED, LIB_PATH, PKVError, last_error  # noqa: F401
+from .api import (  # noqa: F401
+    BlockManager,
+    new_pools,
+    paged_attention_decode,
+    paged_attention_default_partition,
+    paged_attention_workspace_bytes,
+    paged_kv_append,
+    paged_kv_copy_blocks,
+    pool_shapes,
+)
+from .cache import PagedKVCache  # noqa: F401

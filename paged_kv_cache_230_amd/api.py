@@ -1,0 +1,260 @@
+"""Python binding: the C-ABI entry points with torch tensors as arguments.
+
+Each function checks shapes/dtypes/devices of the tensors, takes their data
+pointers and the current HIP stream, and calls the library function of the
+same name.  No computation of the method happens here.  Pool shapes follow
+the storage format of include/pagedkv.h:
+
+    K pool: [num_blocks][num_kv_heads][head_dim // x][block_size][x]
+    V pool: [num_blocks][num_kv_heads][head_dim][block_size]
+    x = 16 // element size (4 for float32, 8 for bfloat16)
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+
+import numpy as np
+import torch
+
+from . import _native as N
+
+__all__ = [
+    "pool_shapes",
+    "new_pools",
+    "paged_kv_append",
+    "paged_kv_copy_blocks",
+    "paged_attention_decode",
+    "paged_attention_workspace_bytes",
+    "paged_attention_default_partition",
+    "BlockManager",
+]
+
+_DT = {torch.float32: N.PKV_F32, torch.bfloat16: N.PKV_BF16}
+
+
+def _dt(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+    return _DT[t]
+
+
+def _stream(device: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return C.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def pool_shapes(num_blocks, num_kv_heads, head_dim, block_size, dtype):
+    x = 16 // torch.empty((), dtype=dtype).element_size()
+    return ((num_blocks, num_kv_heads, head_dim // x, block_size, x), (num_blocks, num_kv_heads, head_dim, block_size))
+
+
+def new_pools(num_blocks, num_kv_heads, head_dim, block_size, dtype, device="cuda"):
+    ks, vs = pool_shapes(num_blocks, num_kv_heads, head_dim, block_size, dtype)
+    return torch.zeros(ks, dtype=dtype, device=device), torch.zeros(vs, dtype=dtype, device=device)
+
+
+def _pool_dims(k_cache, v_cache):
+    _need(k_cache, "k_cache", ndim=5)
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, device=k_cache.device, ndim=4)
+    nb, H, nch, bs, x = k_cache.shape
+    d = nch * x
+    if tuple(v_cache.shape) != (nb, H, d, bs):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} does not match k_cache {tuple(k_cache.shape)}")
+    if x * k_cache.element_size() != 16:
+        raise ValueError("k_cache last dim must span 16 bytes")
+    return nb, H, d, bs
+
+
+def paged_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping):
+    """Write each new token's K/V into its slot (slot < 0 skips)."""
+    nb, H, d, bs = _pool_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _need(k_new, "k_new", k_cache.dtype, dev, 3)
+    _need(v_new, "v_new", k_cache.dtype, dev, 3)
+    _need(slot_mapping, "slot_mapping", torch.int32, dev, 1)
+    T = k_new.shape[0]
+    if tuple(k_new.shape) != (T, H, d) or tuple(v_new.shape) != (T, H, d) or slot_mapping.shape[0] != T:
+        raise ValueError("k_new/v_new must be [T][num_kv_heads][head_dim] with T slots")
+    N.check(
+        N.lib.paged_kv_append(
+            _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, H, d, bs, nb,
+            _dt(k_cache.dtype), _stream(dev),
+        )
+    )
+
+
+def paged_kv_copy_blocks(k_cache, v_cache, src_dst):
+    """Copy whole blocks ``pool[dst] = pool[src]`` for each row of ``src_dst`` ([n][2] int32)."""
+    nb, H, d, bs = _pool_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _need(src_dst, "src_dst", torch.int32, dev, 2)
+    if src_dst.shape[1] != 2:
+        raise ValueError("src_dst must be [num_pairs][2]")
+    N.check(
+        N.lib.paged_kv_copy_blocks(
+            _ptr(k_cache), _ptr(v_cache), _ptr(src_dst), src_dst.shape[0], H, d, bs, nb, _dt(k_cache.dtype),
+            _stream(dev),
+        )
+    )
+
+
+def paged_attention_default_partition(num_seqs, num_kv_heads, head_dim, block_size, max_context_len):
+    return N.check(N.lib.paged_attention_default_partition(num_seqs, num_kv_heads, head_dim, block_size,
+                                                           max_context_len))
+
+
+def paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                                    partition_size=0):
+    n = N.lib.paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                              max_context_len, partition_size)
+    if n == 0 and N.last_error():
+        raise N.PKVError(N.PKV_ERR_INVALID_ARG, N.last_error())
+    return n
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,
+                           partition_size=0, workspace=None):
+    """Decode attention; writes ``out`` ([S][H_q][d], dtype of q) and returns it.
+
+    ``workspace`` is a uint8 device tensor of at least
+    ``paged_attention_workspace_bytes(...)`` bytes; allocated with torch
+    when omitted.
+    """
+    nb, H, d, bs = _pool_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    _need(out, "out", k_cache.dtype, dev, 3)
+    _need(block_tables, "block_tables", torch.int32, dev, 2)
+    _need(context_lens, "context_lens", torch.int32, dev, 1)
+    S, Hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (S, Hq, d):
+        raise ValueError("q/out must be [num_seqs][num_q_heads][head_dim]")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables/context_lens must have num_seqs rows")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = paged_attention_workspace_bytes(S, Hq, H, d, bs, int(max_context_len), partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev, 1)
+    N.check(
+        N.lib.paged_attention_decode(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, Hq, H, d,
+            bs, nb, block_tables.shape[1], int(max_context_len), float(scale), int(partition_size), _ptr(workspace),
+            workspace.numel() if workspace is not None else 0, _dt(k_cache.dtype), _stream(dev),
+        )
+    )
+    return out
+
+
+def _i64p(a: np.ndarray):
+    return a.ctypes.data_as(C.POINTER(C.c_int64))
+
+
+def _i32p(a: np.ndarray | None):
+    return a.ctypes.data_as(C.POINTER(C.c_int32)) if a is not None else None
+
+
+class BlockManager:
+    """Host block manager (pkv_bm_*): free pool, refcounts, fork, copy-on-write."""
+
+    def __init__(self, num_blocks: int, block_size: int, initial_free_order=None):
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        order = None
+        if initial_free_order is not None:
+            order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+            if order.shape != (self.num_blocks,):
+                raise ValueError("initial_free_order must have num_blocks entries")
+        h = C.c_void_p()
+        N.check(N.lib.pkv_bm_create(self.num_blocks, self.block_size, _i32p(order), C.byref(h)))
+        self._h = h
+        self._destroy = N.lib.pkv_bm_destroy  # kept so __del__ works during interpreter shutdown
+        self._slots = np.empty(0, np.int32)
+        self._pairs = np.empty(0, np.int32)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add_seq(self, seq_id: int):
+        N.check(N.lib.pkv_bm_add_seq(self._h, int(seq_id)))
+
+    def fork(self, parent: int, child: int, num_tokens: int):
+        N.check(N.lib.pkv_bm_fork(self._h, int(parent), int(child), int(num_tokens)))
+
+    def free_seq(self, seq_id: int):
+        N.check(N.lib.pkv_bm_free_seq(self._h, int(seq_id)))
+
+    def append_slots(self, seq_ids, num_tokens=None):
+        """Returns ``(slots int32[T], cow_pairs int32[n][2])`` (NumPy views valid until the next call)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        nt = None if num_tokens is None else np.ascontiguousarray(num_tokens, dtype=np.int32)
+        total = n if nt is None else int(nt.sum())
+        if self._slots.shape[0] < max(total, 1):
+            self._slots = np.empty(max(total, 1), np.int32)
+        cow_cap = n
+        if self._pairs.shape[0] < 2 * max(cow_cap, 1):
+            self._pairs = np.empty(2 * max(cow_cap, 1), np.int32)
+        ns, nc = C.c_int32(0), C.c_int32(0)
+        N.check(
+            N.lib.pkv_bm_append_slots(
+                self._h, _i64p(ids), n, _i32p(nt), _i32p(self._slots), self._slots.shape[0], C.byref(ns),
+                _i32p(self._pairs), self._pairs.shape[0] // 2, C.byref(nc),
+            )
+        )
+        return self._slots[: ns.value], self._pairs[: 2 * nc.value].reshape(-1, 2)
+
+    def block_tables(self, seq_ids, max_blocks_per_seq: int, tables_out=None, lens_out=None):
+        """Fill (or allocate) int32 ``[n][max_blocks]`` tables padded with -1 and ``[n]`` lengths."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        if tables_out is None:
+            tables_out = np.empty((n, max_blocks_per_seq), np.int32)
+        if lens_out is None:
+            lens_out = np.empty(n, np.int32)
+        assert tables_out.dtype == np.int32 and tables_out.flags.c_contiguous and tables_out.shape == (n, max_blocks_per_seq)
+        assert lens_out.dtype == np.int32 and lens_out.flags.c_contiguous and lens_out.shape == (n,)
+        N.check(N.lib.pkv_bm_block_tables(self._h, _i64p(ids), n, max_blocks_per_seq, _i32p(tables_out),
+                                          _i32p(lens_out)))
+        return tables_out, lens_out
+
+    def num_free(self) -> int:
+        return N.check(N.lib.pkv_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return N.check(N.lib.pkv_bm_refcount(self._h, int(block)))
+
+    def seq_len(self, seq_id: int) -> int:
+        return N.check(N.lib.pkv_bm_seq_len(self._h, int(seq_id)))
+
+    def num_seqs(self) -> int:
+        return N.check(N.lib.pkv_bm_num_seqs(self._h))
+
+    def free_stack(self) -> list[int]:
+        buf = np.empty(max(self.num_free(), 1), np.int32)
+        n = N.check(N.lib.pkv_bm_free_stack(self._h, _i32p(buf), buf.shape[0]))
+        return buf[:n].tolist()

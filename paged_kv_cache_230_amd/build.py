@@ -1,0 +1,63 @@
+"""Build libpagedkv.so in-tree with hipcc for gfx950.
+
+``python -m paged_kv_cache_230_amd.build`` (or ``build()``) compiles the HIP
+kernels and the host block manager into one shared library next to this
+file.  The build always recompiles; the output is replaced atomically.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libpagedkv.so"
+SOURCES = ["csrc/pagedkv_kernels.hip", "csrc/block_manager.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libpagedkv)")
+
+
+def command(out_path: str) -> list[str]:
+    return [
+        hipcc(),
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        "-Wall",
+        # keep the compiler from forming packed fp32 VALU ops
+        "-Xclang",
+        "-target-feature",
+        "-Xclang",
+        "-packed-fp32-ops",
+        *[os.path.join(HERE, s) for s in SOURCES],
+        "-o",
+        out_path,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    out = os.path.join(HERE, LIB_NAME)
+    tmp = out + ".tmp"
+    cmd = command(tmp)
+    res = subprocess.run(cmd, cwd=HERE, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    log = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{log}")
+    if verbose and log.strip():
+        print(log, file=sys.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

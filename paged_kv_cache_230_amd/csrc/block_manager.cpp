@@ -1,0 +1,272 @@
+// Host block manager: free pool, per-block reference counts, block tables,
+// fork (prefix sharing) and copy-on-write.
+//
+// What the pages fix ("PagedAttention" robocikowo.com, Komponenty and Jak
+// działa; "PagedAttention et RadixAttention : parlons de KV Cache", section
+// on PagedAttention as an operating system, steps 1-4): a per-sequence table
+// maps logical blocks to physical ones; a manager hands blocks out of a free
+// pool as sequences grow, one block at a time; sequences with a common
+// prefix point at the same physical blocks, counted by reference, and a
+// write into a shared block first duplicates it; a finished sequence gives
+// its blocks back individually for immediate reuse ("PagedAttention —
+// Gestion mémoire pour LLM à long contexte", Pourquoi c'est important).
+//
+// The pages leave the policy open; this manager is deterministic:
+//   * the free pool is a stack (vector back = top); the caller's initial
+//     order hands out element 0 first; released blocks are pushed on top;
+//   * a write at length L allocates at block boundaries, and copies the
+//     block holding slot L only if it is shared; the batch is walked in
+//     call order;
+//   * every call validates and counts what it needs before mutating, so an
+//     error leaves the state unchanged.
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "pkv_status.h"
+
+struct pkv_block_manager {
+  struct Seq {
+    std::vector<int32_t> table;
+    int32_t len = 0;
+  };
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_stack;  // back() is handed out next
+  std::vector<int32_t> refcount;
+  std::unordered_map<int64_t, Seq> seqs;
+};
+
+namespace {
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int32_t check_handle(const pkv_block_manager* bm) {
+  if (!bm) return pkv::fail(PKV_ERR_INVALID_ARG, "null block manager handle");
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order,
+                      pkv_block_manager** out) {
+  if (!out) return pkv::fail(PKV_ERR_INVALID_ARG, "out handle pointer is null");
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_blocks (%d) and block_size (%d) must be positive", num_blocks,
+                     block_size);
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_blocks * block_size exceeds the int32 slot range");
+  auto* bm = new (std::nothrow) pkv_block_manager();
+  if (!bm) return pkv::fail(PKV_ERR_INVALID_ARG, "out of host memory");
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->refcount.assign(num_blocks, 0);
+  bm->free_stack.resize(num_blocks);
+  if (initial_free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = initial_free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete bm;
+        return pkv::fail(PKV_ERR_INVALID_ARG, "initial_free_order is not a permutation (entry %d = %d)", i, b);
+      }
+      seen[b] = 1;
+      bm->free_stack[num_blocks - 1 - i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) bm->free_stack[num_blocks - 1 - i] = i;
+  }
+  *out = bm;
+  return pkv::ok();
+}
+
+void pkv_bm_destroy(pkv_block_manager* bm) { delete bm; }
+
+int32_t pkv_bm_add_seq(pkv_block_manager* bm, int64_t seq_id) {
+  if (int32_t e = check_handle(bm)) return e;
+  if (bm->seqs.count(seq_id)) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %lld already exists", (long long)seq_id);
+  bm->seqs.emplace(seq_id, pkv_block_manager::Seq{});
+  return pkv::ok();
+}
+
+int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child, int32_t num_tokens) {
+  if (int32_t e = check_handle(bm)) return e;
+  auto it = bm->seqs.find(parent);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown parent sequence %lld", (long long)parent);
+  if (bm->seqs.count(child)) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %lld already exists", (long long)child);
+  if (num_tokens < 0 || num_tokens > it->second.len)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "fork length %d outside the parent's context [0, %d]", num_tokens,
+                     it->second.len);
+  pkv_block_manager::Seq s;
+  const int64_t nshared = cdiv(num_tokens, bm->block_size);
+  s.table.assign(it->second.table.begin(), it->second.table.begin() + nshared);
+  s.len = num_tokens;
+  for (int32_t b : s.table) bm->refcount[b] += 1;
+  bm->seqs.emplace(child, std::move(s));
+  return pkv::ok();
+}
+
+int32_t pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs,
+                            const int32_t* num_tokens, int32_t* slot_mapping_out, int32_t slot_capacity,
+                            int32_t* n_slots_out, int32_t* cow_pairs_out, int32_t cow_capacity,
+                            int32_t* n_cow_out) {
+  if (int32_t e = check_handle(bm)) return e;
+  if (n_seqs < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "n_seqs < 0");
+  if (n_seqs > 0 && !seq_ids) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_ids is null");
+  if (slot_capacity < 0 || cow_capacity < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "negative capacity");
+  const int32_t bs = bm->block_size;
+
+  // Pass 1: validate and count, without touching the state.
+  std::vector<pkv_block_manager::Seq*> seqp(n_seqs);
+  std::unordered_set<int64_t> seen;
+  seen.reserve(static_cast<size_t>(n_seqs) * 2);
+  int64_t total_tokens = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    if (!seen.insert(seq_ids[i]).second)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %lld appears twice in one call", (long long)seq_ids[i]);
+    const int32_t n = num_tokens ? num_tokens[i] : 1;
+    if (n < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "negative token count for sequence %lld", (long long)seq_ids[i]);
+    if (static_cast<int64_t>(it->second.len) + n > INT32_MAX)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %lld would exceed the int32 length range", (long long)seq_ids[i]);
+    seqp[i] = &it->second;
+    total_tokens += n;
+  }
+  if (total_tokens > slot_capacity)
+    return pkv::fail(PKV_ERR_CAPACITY, "slot buffer holds %d slots, %lld needed", slot_capacity, (long long)total_tokens);
+  if (total_tokens > 0 && !slot_mapping_out) return pkv::fail(PKV_ERR_INVALID_ARG, "slot_mapping_out is null");
+  int64_t need_blocks = 0, need_cow = 0;
+  std::unordered_map<int32_t, int32_t> dropped;  // simulated refcount drops on shared last blocks
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t n = num_tokens ? num_tokens[i] : 1;
+    if (n == 0) continue;
+    const int32_t L = seqp[i]->len;
+    if (L % bs) {
+      const int32_t last = seqp[i]->table[L / bs];
+      int32_t& d = dropped[last];
+      if (bm->refcount[last] - d > 1) {
+        ++need_cow;
+        ++d;
+      }
+    }
+    need_blocks += cdiv(static_cast<int64_t>(L) + n, bs) - cdiv(L, bs);
+  }
+  need_blocks += need_cow;
+  if (need_cow > cow_capacity)
+    return pkv::fail(PKV_ERR_CAPACITY, "copy-pair buffer holds %d pairs, %lld needed", cow_capacity, (long long)need_cow);
+  if (need_cow > 0 && !cow_pairs_out) return pkv::fail(PKV_ERR_INVALID_ARG, "cow_pairs_out is null");
+  if (need_blocks > static_cast<int64_t>(bm->free_stack.size()))
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "%lld blocks needed, %zu free", (long long)need_blocks,
+                     bm->free_stack.size());
+
+  // Pass 2: apply.  Cannot fail from here on.
+  int32_t ns = 0, nc = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    pkv_block_manager::Seq& s = *seqp[i];
+    const int32_t n = num_tokens ? num_tokens[i] : 1;
+    for (int32_t t = 0; t < n; ++t) {
+      const int32_t L = s.len;
+      if (L % bs == 0) {
+        const int32_t b = bm->free_stack.back();
+        bm->free_stack.pop_back();
+        bm->refcount[b] = 1;
+        s.table.push_back(b);
+      } else {
+        const int32_t old = s.table[L / bs];
+        if (bm->refcount[old] > 1) {
+          const int32_t b = bm->free_stack.back();
+          bm->free_stack.pop_back();
+          cow_pairs_out[2 * nc] = old;
+          cow_pairs_out[2 * nc + 1] = b;
+          ++nc;
+          bm->refcount[old] -= 1;
+          bm->refcount[b] = 1;
+          s.table[L / bs] = b;
+        }
+      }
+      slot_mapping_out[ns++] = s.table[L / bs] * bs + L % bs;
+      s.len = L + 1;
+    }
+  }
+  if (n_slots_out) *n_slots_out = ns;
+  if (n_cow_out) *n_cow_out = nc;
+  return pkv::ok();
+}
+
+int32_t pkv_bm_free_seq(pkv_block_manager* bm, int64_t seq_id) {
+  if (int32_t e = check_handle(bm)) return e;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  for (int32_t b : it->second.table) {
+    if (--bm->refcount[b] == 0) bm->free_stack.push_back(b);
+  }
+  bm->seqs.erase(it);
+  return pkv::ok();
+}
+
+int32_t pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs,
+                            int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out) {
+  if (int32_t e = check_handle(bm)) return e;
+  if (n_seqs < 0 || max_blocks_per_seq < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (n_seqs > 0 && (!seq_ids || (!tables_out && max_blocks_per_seq > 0)))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "null seq_ids or tables_out");
+  std::vector<const pkv_block_manager::Seq*> seqp(n_seqs);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    if (static_cast<int64_t>(it->second.table.size()) > max_blocks_per_seq)
+      return pkv::fail(PKV_ERR_CAPACITY, "sequence %lld holds %zu blocks > max_blocks_per_seq %d",
+                       (long long)seq_ids[i], it->second.table.size(), max_blocks_per_seq);
+    seqp[i] = &it->second;
+  }
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    int32_t* row = tables_out + static_cast<int64_t>(i) * max_blocks_per_seq;
+    const auto& t = seqp[i]->table;
+    std::copy(t.begin(), t.end(), row);
+    std::fill(row + t.size(), row + max_blocks_per_seq, -1);
+    if (context_lens_out) context_lens_out[i] = seqp[i]->len;
+  }
+  return pkv::ok();
+}
+
+int32_t pkv_bm_num_free(const pkv_block_manager* bm) {
+  if (int32_t e = check_handle(bm)) return e;
+  return static_cast<int32_t>(bm->free_stack.size());
+}
+
+int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block) {
+  if (int32_t e = check_handle(bm)) return e;
+  if (block < 0 || block >= bm->num_blocks)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "block %d outside [0, %d)", block, bm->num_blocks);
+  return bm->refcount[block];
+}
+
+int32_t pkv_bm_seq_len(const pkv_block_manager* bm, int64_t seq_id) {
+  if (int32_t e = check_handle(bm)) return e;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  return it->second.len;
+}
+
+int32_t pkv_bm_num_seqs(const pkv_block_manager* bm) {
+  if (int32_t e = check_handle(bm)) return e;
+  return static_cast<int32_t>(bm->seqs.size());
+}
+
+int32_t pkv_bm_free_stack(const pkv_block_manager* bm, int32_t* out, int32_t capacity) {
+  if (int32_t e = check_handle(bm)) return e;
+  const int32_t n = static_cast<int32_t>(bm->free_stack.size());
+  if (capacity < n) return pkv::fail(PKV_ERR_CAPACITY, "capacity %d < %d free blocks", capacity, n);
+  if (n > 0 && !out) return pkv::fail(PKV_ERR_INVALID_ARG, "out is null");
+  std::copy(bm->free_stack.begin(), bm->free_stack.end(), out);
+  return n;
+}
+
+}  // extern "C"

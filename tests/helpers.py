@@ -1,0 +1,88 @@
+"""Shared helpers for the parity tests: run a workload through the HIP
+library, convert storage, and compare against the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+# Tolerances of the decode output against the fp64 oracle.
+#   fp32 inputs: max abs error <= 1e-5.
+#   bf16 inputs with fp32 accumulation: max abs error <= 2e-3 and max
+#   relative error <= 1e-2, relative error measured per element against
+#   max(|ref|, tau) with tau = 1e-3 * max|ref| over the batch (a floor that
+#   keeps near-zero reference values from turning rounding into "100 %").
+TOL = {"f32": dict(abs=1e-5, rel=None), "bf16": dict(abs=2e-3, rel=1e-2)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def storage_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError(t.dtype)
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint16) if a.dtype == np.uint16 else a.view(np.uint32)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def errors(got: torch.Tensor, ref: np.ndarray):
+    g = to_f64(got)
+    err = np.abs(g - ref)
+    tau = 1e-3 * float(np.abs(ref).max()) if ref.size else 0.0
+    rel = err / np.maximum(np.abs(ref), max(tau, 1e-300))
+    normrel = float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-300))
+    finite = bool(np.isfinite(g).all())
+    return float(err.max(initial=0.0)), float(rel.max(initial=0.0)), normrel, finite
+
+
+def assert_close(got, ref, dtype, what=""):
+    mabs, mrel, nrel, finite = errors(got, ref)
+    tol = TOL[dtype]
+    say(f"  parity {what}: max_abs={mabs:.3e} max_rel={mrel:.3e} norm_rel={nrel:.3e}")
+    assert finite, f"{what}: non-finite output"
+    assert mabs <= tol["abs"], f"{what}: max abs error {mabs} > {tol['abs']}"
+    if tol["rel"] is not None:
+        assert mrel <= tol["rel"], f"{what}: max rel error {mrel} > {tol['rel']}"
+
+
+def product_cache(w, device="cuda"):
+    """Play a workload's setup script through the library; returns a PagedKVCache."""
+    from paged_kv_cache_230_amd import PagedKVCache
+
+    c = w.config
+    cache = PagedKVCache(w.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.torch_dtype, device,
+                         w.free_order)
+    for op in w.setup_ops:
+        cache.apply(op, w.kv)
+    torch.cuda.synchronize()
+    return cache
+
+
+def product_step(cache, w, k, partition_size=0):
+    """Decode step k through the library: append one token per sequence, then decode."""
+    kn, vn = w.kv(("step", k))
+    slots, pairs = cache.append(w.decode_seqs, [1] * w.num_seqs, kn, vn)
+    q = w.q(k).to(cache.device)
+    out = cache.decode(q, w.decode_seqs, partition_size=partition_size)
+    torch.cuda.synchronize()
+    return out, slots, pairs
+
+
+def assert_pools_equal(cache, run):
+    kg, vg = storage_np(cache.k_cache), storage_np(cache.v_cache)
+    assert kg.shape == run.k_pool.shape and vg.shape == run.v_pool.shape
+    assert np.array_equal(bits(kg), bits(run.k_pool)), "K pool differs from the oracle's"
+    assert np.array_equal(bits(vg), bits(run.v_pool)), "V pool differs from the oracle's"

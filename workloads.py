@@ -175,7 +175,7 @@ class Workload:
         lengths = self._lengths_override(lengths)
         bs = self.config.block_size
         used = int(sum((int(L) - 1 + bs - 1) // bs for L in lengths))
-        num_blocks = int(math.ceil(used / 0.95)) + 1
+        num_blocks = int(math.ceil(used / 0.95))
         self._finish_plain(rng, lengths, num_blocks)
 
     def _build_prefix(self, rng):
@@ -228,7 +228,9 @@ class Workload:
             x = x * std
         return x
 
-    def _kv_scale(self) -> float:
+    def _k_scale(self) -> float:
+        # "large": keys x32 with queries x512 give logits with a standard
+        # deviation near 130; values keep the configuration's distribution.
         return 32.0 if self.variant == "large" else 1.0
 
     def _q_scale(self) -> float:
@@ -248,9 +250,8 @@ class Workload:
         else:
             raise KeyError(key)
         shape = (T, c.num_kv_heads, c.head_dim)
-        std = c.value_std * self._kv_scale()
-        k = self._randn(key + (0,), shape, std)
-        v = self._randn(key + (1,), shape, std)
+        k = self._randn(key + (0,), shape, c.value_std * self._k_scale())
+        v = self._randn(key + (1,), shape, c.value_std)
         if self.variant == "needle" and key[0] == "prefill" and T > 0:
             # Plant, in every kv head, a key equal to 8x the first query head
             # of its group (step-0 query) at one seeded position.
