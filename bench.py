@@ -118,7 +118,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3_70b_32k_bf16")
-    ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = library default)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="about this many tokens per decode workgroup (0 = one round of resident workgroups)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences in the oracle sample (default: all)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -166,8 +167,8 @@ def main():
     bs = c.block_size
     max_len_bound = int(max(bm.seq_len(int(s)) for s in seqs)) + nsteps
     max_blocks = -(-max_len_bound // bs)
-    P = args.partition if args.partition else pkv.paged_attention_default_partition(
-        S, c.num_kv_heads, c.head_dim, bs, max_len_bound)
+    P = args.partition
+    wph = pkv.paged_attention_workgroups_per_head(S, c.num_kv_heads, c.head_dim, bs, max_len_bound, P, c.torch_dtype)
     ws_bytes = pkv.paged_attention_workspace_bytes(S, c.num_q_heads, c.num_kv_heads, c.head_dim, bs, max_len_bound, P)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty(S, c.num_q_heads, c.head_dim, dtype=c.torch_dtype, device=dev)
@@ -285,6 +286,7 @@ def main():
             "block_size": bs,
             "num_blocks": w.num_blocks,
             "partition_size": P,
+            "decode_workgroups": wph * c.num_kv_heads,
         },
         "tokens_per_s": round(S * args.steps / elapsed, 1),
         "pct_hbm_peak_whole_step": round(100.0 * value * 1e9 / HBM_PEAK, 2),

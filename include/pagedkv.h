@@ -133,15 +133,26 @@ int32_t paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ds
 /* max_context_len : host upper bound on context_lens, <=                 */
 /*                 max_blocks_per_seq * block_size                        */
 /* scale         : logit scale (usually 1/sqrt(head_dim))                 */
-/* partition_size: tokens per context partition (a multiple of            */
-/*                 block_size) -- each (sequence, kv head, partition) is  */
-/*                 one workgroup, partitions are merged by log-sum-exp;   */
-/*                 0 picks paged_attention_default_partition()            */
-/* workspace     : device scratch for partition partials, at least        */
+/* partition_size: 0 (default) splits the work over one round of the     */
+/*                 workgroups the GPU holds at once; > 0 asks for about   */
+/*                 that many tokens per workgroup (num_seqs *             */
+/*                 max_context_len / partition_size workgroups per kv     */
+/*                 head; a value >= that product means one workgroup per  */
+/*                 kv head and no sequence is split).  Results differ     */
+/*                 only by fp32 rounding between splits.                  */
+/* workspace     : device scratch, at least                               */
 /*                 paged_attention_workspace_bytes(...) bytes, 256-byte   */
-/*                 aligned; may be NULL when that size is 0.  Its content */
-/*                 is overwritten; calls sharing a workspace must be      */
-/*                 ordered on one stream.                                 */
+/*                 aligned, required whenever num_seqs > 0: it holds the  */
+/*                 per-call work queues, the (sequence, partition) item   */
+/*                 index and the partition partials.  Any content is      */
+/*                 accepted (each call resets what it needs); calls       */
+/*                 sharing a workspace must be ordered on one stream.     */
+/*                                                                        */
+/* Work distribution (balanced split): for each kv head the blocks of all */
+/* sequences form one list of T blocks; each of the N workgroups of that  */
+/* head takes an equal contiguous range of it.  A range covering a whole  */
+/* sequence writes its rows; pieces of a split sequence write partials    */
+/* that a second kernel merges by log-sum-exp.                            */
 int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -149,15 +160,15 @@ int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                                pkv_dtype dt, void* stream);
 
-/* The partition size that partition_size == 0 selects (a multiple of     */
-/* block_size), or a negative status for invalid arguments.               */
-int32_t paged_attention_default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                          int32_t block_size, int32_t max_context_len);
+/* Workgroups per kv head that paged_attention_decode uses for these     */
+/* arguments on the current device, or a negative status.                 */
+int32_t paged_attention_workgroups_per_head(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t block_size, int32_t max_context_len, int32_t partition_size,
+                                            pkv_dtype dt);
 
-/* Workspace bytes paged_attention_decode needs for these arguments (0    */
-/* when every sequence fits one partition).  Returns 0 and sets the last  */
-/* error for invalid arguments (check pkv_last_error() if 0 is            */
-/* unexpected).                                                            */
+/* Workspace bytes paged_attention_decode needs for these arguments on    */
+/* the current device (0 only when num_seqs == 0).  Returns 0 and sets    */
+/* the last error for invalid arguments.                                   */
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                        int32_t partition_size);

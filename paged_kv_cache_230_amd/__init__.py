@@ -10,7 +10,7 @@ from .api import (  # noqa: F401
     BlockManager,
     new_pools,
     paged_attention_decode,
-    paged_attention_default_partition,
+    paged_attention_workgroups_per_head,
     paged_attention_workspace_bytes,
     paged_kv_append,
     paged_kv_copy_blocks,

@@ -26,7 +26,7 @@ __all__ = [
     "paged_kv_copy_blocks",
     "paged_attention_decode",
     "paged_attention_workspace_bytes",
-    "paged_attention_default_partition",
+    "paged_attention_workgroups_per_head",
     "BlockManager",
 ]
 
@@ -115,9 +115,10 @@ def paged_kv_copy_blocks(k_cache, v_cache, src_dst):
     )
 
 
-def paged_attention_default_partition(num_seqs, num_kv_heads, head_dim, block_size, max_context_len):
-    return N.check(N.lib.paged_attention_default_partition(num_seqs, num_kv_heads, head_dim, block_size,
-                                                           max_context_len))
+def paged_attention_workgroups_per_head(num_seqs, num_kv_heads, head_dim, block_size, max_context_len,
+                                        partition_size=0, dtype=torch.bfloat16):
+    return N.check(N.lib.paged_attention_workgroups_per_head(num_seqs, num_kv_heads, head_dim, block_size,
+                                                             max_context_len, partition_size, _dt(dtype)))
 
 
 def paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,

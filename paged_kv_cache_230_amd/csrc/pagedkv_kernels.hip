@@ -33,6 +33,7 @@
 //     accumulator) partials and a merge kernel combines them.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -72,17 +73,18 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_acc;  // [S][Hq][max_parts][D]
-  float* ws_m;    // [S][Hq][max_parts]
-  float* ws_l;    // [S][Hq][max_parts]
+  float* ws_acc;     // [N][2][G][D] partial accumulators (workgroup, slot, head)
+  float* ws_m;       // [N][2][G] partial max (log2 domain)
+  float* ws_l;       // [N][2][G] partial sum
+  int32_t* meta;     // [S][Hkv][2] first workgroup index and number of pieces of (s, g)
+  int32_t wgs_per_head;  // N / Hkv
+  int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
-  int32_t partition_size;
-  int32_t max_parts;
   float scale_log2;  // scale * log2(e)
 };
 
@@ -175,46 +177,69 @@ struct Acc {
   float4v o[D / 16];
 };
 
-template <bool BF16, int D, int BS>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a) {
-  constexpr int GMAX = BF16 ? 8 : 16;
-  constexpr int NT = D / 16;
-  __shared__ float sm_o[kWaves][GMAX][D];
-  __shared__ float sm_m[kWaves][GMAX];
-  __shared__ float sm_l[kWaves][GMAX];
+template <bool BF16, int D>
+struct DecodeSmem {
+  static constexpr int GMAX = BF16 ? 8 : 16;
+  float o[kWaves][GMAX][D];  // per-wave accumulators of the current segment
+  float m[kWaves][GMAX];
+  float l[kWaves][GMAX];
+  float M[GMAX];    // merge: per-head maximum over pieces
+  float inv[GMAX];  // merge: 1 / weighted denominator
+  int wave_sum[kWaves];
+  int found_seq;
+  int found_pre;
+};
 
-  const int p = blockIdx.x;
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
+__device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
+
+// Inclusive prefix sum of one int per thread over the workgroup; *total
+// receives the workgroup total.  All threads must call it.
+template <bool BF16, int D>
+__device__ __forceinline__ int block_scan(int v, int* total, DecodeSmem<BF16, D>& sm) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sm.wave_sum[w] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    before += i < w ? sm.wave_sum[i] : 0;
+    tot += sm.wave_sum[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x;
+}
+
+// Partial row of (workgroup b, slot) for head hh: ((b * 2 + slot) * G + hh).
+// Slot 1 holds a piece that starts at its sequence's first block, slot 0 a
+// piece that starts inside the sequence.
+
+// Blocks [lb0, lb1) of sequence s (length L) for kv head g.  When
+// `prow` < 0 the segment is the whole sequence and the output rows are
+// written; otherwise (max, sum, accumulator) go to partial row `prow`.
+template <bool BF16, int D, int BS>
+__device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0, int lb1, int prow,
+                               DecodeSmem<BF16, D>& sm) {
+  constexpr int NT = D / 16;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15;
   const int quad = lane >> 4;
   const int G = a.group;
   const int Hq = a.num_q_heads;
-  const int P = a.partition_size;
 
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
+  const int start = lb0 * BS;
+  const int end = min(lb1 * BS, L);
+  const int nblk = lb1 - lb0;
+  const int32_t* tbl = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq + lb0;
   const size_t out_row0 = (static_cast<size_t>(s) * Hq + static_cast<size_t>(g) * G) * D;
-
-  if (L == 0) {
-    if (p == 0) {
-      for (int e = threadIdx.x; e < G * D; e += kThreads) {
-        if constexpr (BF16)
-          static_cast<uint16_t*>(a.out)[out_row0 + e] = 0;
-        else
-          static_cast<float*>(a.out)[out_row0 + e] = 0.f;
-      }
-    }
-    return;
-  }
-  const int start = p * P;
-  if (start >= L) return;
-  const int end = min(start + P, L);
-  const int nparts = (L + P - 1) / P;
-  const int nblk = (end - start + BS - 1) / BS;
-  const int32_t* tbl = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq + start / BS;
 
   // Query operand: column `row` = query head g*G + row (zero past G).
   QOperand<BF16, D> qo;
@@ -380,136 +405,202 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
       const int hh = 4 * quad + v;
       if (hh < G && (!BF16 || quad < 2)) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sm_o[w][hh][16 * nt + row] = acc.o[nt][v];
+        for (int nt = 0; nt < NT; ++nt) sm.o[w][hh][16 * nt + row] = acc.o[nt][v];
       }
     }
     if (quad == 0 && row < G) {
-      sm_m[w][row] = m_run;
-      sm_l[w][row] = l_run;
+      sm.m[w][row] = m_run;
+      sm.l[w][row] = l_run;
     }
   }
   __syncthreads();
 
-  const size_t part_row0 = (static_cast<size_t>(s) * Hq + static_cast<size_t>(g) * G) * a.max_parts + p;
   for (int e = threadIdx.x; e < G * D; e += kThreads) {
     const int hh = e / D;
     const int d = e - hh * D;
-    float M = sm_m[0][hh];
-    for (int ww = 1; ww < nw; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    float M = sm.m[0][hh];
+    for (int ww = 1; ww < nw; ++ww) M = fmaxf(M, sm.m[ww][hh]);
     float num = 0.f, den = 0.f;
     for (int ww = 0; ww < nw; ++ww) {
-      const float f = __builtin_amdgcn_exp2f(sm_m[ww][hh] - M);
-      num += f * sm_o[ww][hh][d];
-      den += f * sm_l[ww][hh];
+      const float f = __builtin_amdgcn_exp2f(sm.m[ww][hh] - M);
+      num += f * sm.o[ww][hh][d];
+      den += f * sm.l[ww][hh];
     }
-    if (nparts == 1) {
+    if (prow < 0) {
       const float o = num / den;
       if constexpr (BF16)
         static_cast<uint16_t*>(a.out)[out_row0 + e] = f32_to_bf16_bits(o);
       else
         static_cast<float*>(a.out)[out_row0 + e] = o;
     } else {
-      const size_t pr0 = part_row0 + static_cast<size_t>(hh) * a.max_parts;
-      a.ws_acc[pr0 * D + d] = num;
+      const size_t r = static_cast<size_t>(prow) * G + hh;
+      a.ws_acc[r * D + d] = num;
       if (d == 0) {
-        a.ws_m[pr0] = M;
-        a.ws_l[pr0] = den;
+        a.ws_m[r] = M;
+        a.ws_l[r] = den;
       }
     }
+  }
+  __syncthreads();  // the next segment reuses the LDS
+}
+
+// Balanced split.  For one kv head, the blocks of all sequences form one
+// list of T blocks (sequence after sequence).  Workgroup b serves kv head
+// g = b mod H_kv and takes the contiguous range [k T / N_g, (k+1) T / N_g)
+// of that list, k = b / H_kv: every workgroup gets the same number of
+// blocks whatever the mix of lengths.  Within its range it walks segment by
+// segment (one per sequence touched): a segment that is a whole sequence
+// writes its output rows; a piece of a split sequence writes a partial, and
+// the workgroup holding the sequence's first block records (first
+// workgroup, number of pieces) for the merge kernel.  With 8 kv heads the
+// round-robin dealing of workgroups to the 8 XCDs gives each XCD one head.
+template <bool BF16, int D, int BS>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+  __shared__ DecodeSmem<BF16, D> sm;
+  const int S = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
+  const int b = blockIdx.x;
+  const int g = b % Hkv;
+  const int k = b / Hkv;
+
+  // Total blocks per head.
+  int T = 0;
+  for (int base = 0; base < S; base += kThreads) {
+    const int s = base + threadIdx.x;
+    const int nb = s < S ? (clamp_len(a.context_lens[s], a.max_context_len) + BS - 1) / BS : 0;
+    int tot;
+    block_scan<BF16, D>(nb, &tot, sm);
+    T += tot;
+  }
+  const int Ng = a.wgs_per_head < T ? a.wgs_per_head : T;  // at least one block per workgroup
+  if (k >= Ng) return;
+  const int64_t b0 = static_cast<int64_t>(k) * T / Ng;
+  const int64_t b1 = static_cast<int64_t>(k + 1) * T / Ng;
+
+  // First sequence touched: prefix(s) <= b0 < prefix(s) + nb(s).
+  int s = 0, pre = 0, run = 0;
+  for (int base = 0; base < S; base += kThreads) {
+    if (threadIdx.x == 0) sm.found_seq = -1;
+    const int sq = base + threadIdx.x;
+    const int nb = sq < S ? (clamp_len(a.context_lens[sq], a.max_context_len) + BS - 1) / BS : 0;
+    int tot;
+    const int incl = run + block_scan<BF16, D>(nb, &tot, sm);
+    if (sq < S && nb > 0 && incl > b0 && incl - nb <= b0) {
+      sm.found_seq = sq;
+      sm.found_pre = incl - nb;
+    }
+    __syncthreads();
+    const int fs = sm.found_seq;
+    const int fp = sm.found_pre;
+    __syncthreads();
+    if (fs >= 0) {
+      s = fs;
+      pre = fp;
+      break;
+    }
+    run += tot;
+  }
+
+  // Walk the segments of [b0, b1).
+  for (; s < S && pre < b1; ++s) {
+    const int L = clamp_len(a.context_lens[s], a.max_context_len);
+    const int nb = (L + BS - 1) / BS;
+    if (nb == 0) continue;
+    const int lb0 = static_cast<int>((b0 > pre ? b0 : pre) - pre);
+    const int lb1 = static_cast<int>((b1 < static_cast<int64_t>(pre) + nb ? b1 : static_cast<int64_t>(pre) + nb) - pre);
+    const bool whole = lb0 == 0 && lb1 == nb;
+    const int prow = whole ? -1 : (b * 2 + (lb0 == 0 ? 1 : 0));
+    decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, sm);
+    if (lb0 == 0 && threadIdx.x == 0) {
+      // Workgroup (within this head) holding block x of the list: the largest
+      // k' with k' T / Ng <= x.
+      const int64_t last = pre + nb - 1;
+      const int k_last = static_cast<int>(((last + 1) * Ng - 1) / T);
+      int32_t* mt = a.meta + (static_cast<size_t>(s) * Hkv + g) * 2;
+      mt[0] = k;
+      mt[1] = k_last - k + 1;
+    }
+    pre += nb;
   }
 }
 
-// Log-sum-exp merge of the partition partials of sequences with more than
-// one partition.  One workgroup per (kv head, sequence) merges its G query
-// heads: first the per-head maximum and weighted denominator over the
-// partitions, then the weighted sum of the accumulator rows, read as
-// coalesced 16-byte loads (one accumulator row is D contiguous floats).
+// Log-sum-exp merge of the pieces of split sequences, and zero rows for
+// empty ones.  One workgroup per (kv head, sequence); runs as its own
+// launch, so every partial written by the decode kernel is visible.
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int GMAX = BF16 ? 8 : 16;
-  __shared__ float sm_M[GMAX];
-  __shared__ float sm_inv[GMAX];
+  __shared__ DecodeSmem<BF16, D> sm;
   const int g = blockIdx.x;
   const int s = blockIdx.y;
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
-  const int P = a.partition_size;
-  const int nparts = (L + P - 1) / P;
-  if (nparts <= 1) return;
   const int G = a.group;
-  const int mp = a.max_parts;
+  const int Hkv = a.num_kv_heads;
   const size_t head0 = static_cast<size_t>(s) * a.num_q_heads + static_cast<size_t>(g) * G;
+  const int L = clamp_len(a.context_lens[s], a.max_context_len);
+  if (L == 0) {
+    for (int e = threadIdx.x; e < G * D; e += kThreads) {
+      if constexpr (BF16)
+        static_cast<uint16_t*>(a.out)[head0 * D + e] = 0;
+      else
+        static_cast<float*>(a.out)[head0 * D + e] = 0.f;
+    }
+    return;
+  }
+  const int32_t* mt = a.meta + (static_cast<size_t>(s) * Hkv + g) * 2;
+  const int first = mt[0];
+  const int npieces = mt[1];
+  if (npieces <= 1) return;
+  // Partial row of piece j: workgroup (first + j) of head g; slot 1 for the
+  // first piece (it starts at the sequence's first block), slot 0 after.
+  auto prow = [&](int j) { return ((first + j) * Hkv + g) * 2 + (j == 0 ? 1 : 0); };
 
-  // Phase 1: per head, M = max_p m_p and den = sum_p 2^(m_p - M) l_p.
-  // 16 threads per head (a quarter wave), strided over the partitions.
+  // Phase 1: per head, M = max_j m_j and den = sum_j 2^(m_j - M) l_j; 16 threads per head.
   {
-    const int hh = threadIdx.x >> 4;
+    const int h = threadIdx.x >> 4;
     const int sub = threadIdx.x & 15;
-    for (int h0 = 0; h0 < G; h0 += kThreads / 16) {
-      const int h = h0 + hh;
-      const bool live = h < G;
-      const float* mrow = a.ws_m + (head0 + (live ? h : 0)) * mp;
-      const float* lrow = a.ws_l + (head0 + (live ? h : 0)) * mp;
-      float M = -INFINITY;
-      if (live)
-        for (int p = sub; p < nparts; p += 16) M = fmaxf(M, mrow[p]);
+    const bool live = h < G;
+    float M = -INFINITY;
+    if (live)
+      for (int j = sub; j < npieces; j += 16) M = fmaxf(M, a.ws_m[static_cast<size_t>(prow(j)) * G + h]);
 #pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
-      float den = 0.f;
-      if (live)
-        for (int p = sub; p < nparts; p += 16) den += __builtin_amdgcn_exp2f(mrow[p] - M) * lrow[p];
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) den += __shfl_xor(den, off, 16);
-      if (live && sub == 0) {
-        sm_M[h] = M;
-        sm_inv[h] = 1.f / den;
+    for (int off = 8; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
+    float den = 0.f;
+    if (live)
+      for (int j = sub; j < npieces; j += 16) {
+        const size_t r = static_cast<size_t>(prow(j)) * G + h;
+        den += __builtin_amdgcn_exp2f(a.ws_m[r] - M) * a.ws_l[r];
       }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) den += __shfl_xor(den, off, 16);
+    if (live && sub == 0) {
+      sm.M[h] = M;
+      sm.inv[h] = 1.f / den;
     }
   }
   __syncthreads();
-
   // Phase 2: each thread owns 4 consecutive dims of one head.
   for (int e = threadIdx.x * 4; e < G * D; e += kThreads * 4) {
     const int h = e / D;
     const int d = e - h * D;
-    const float M = sm_M[h];
-    const float* mrow = a.ws_m + (head0 + h) * mp;
-    const float* arow = a.ws_acc + (head0 + h) * mp * D + d;
+    const float M = sm.M[h];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int p = 0;
-    for (; p + 4 <= nparts; p += 4) {
-      float4 v[4];
-      float f[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = *reinterpret_cast<const float4*>(arow + static_cast<size_t>(p + i) * D);
-        f[i] = __builtin_amdgcn_exp2f(mrow[p + i] - M);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc.x += f[i] * v[i].x;
-        acc.y += f[i] * v[i].y;
-        acc.z += f[i] * v[i].z;
-        acc.w += f[i] * v[i].w;
-      }
-    }
-    for (; p < nparts; ++p) {
-      const float4 v = *reinterpret_cast<const float4*>(arow + static_cast<size_t>(p) * D);
-      const float f = __builtin_amdgcn_exp2f(mrow[p] - M);
+    for (int j = 0; j < npieces; ++j) {
+      const size_t r = static_cast<size_t>(prow(j)) * G + h;
+      const float f = __builtin_amdgcn_exp2f(a.ws_m[r] - M);
+      const float4 v = *reinterpret_cast<const float4*>(a.ws_acc + r * D + d);
       acc.x += f * v.x;
       acc.y += f * v.y;
       acc.z += f * v.z;
       acc.w += f * v.w;
     }
-    const float inv = sm_inv[h];
+    const float inv = sm.inv[h];
     const size_t o = (head0 + h) * D + d;
-    const float r[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    const float r4[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (BF16)
-        static_cast<uint16_t*>(a.out)[o + i] = f32_to_bf16_bits(r[i]);
+        static_cast<uint16_t*>(a.out)[o + i] = f32_to_bf16_bits(r4[i]);
       else
-        static_cast<float*>(a.out)[o + i] = r[i];
+        static_cast<float*>(a.out)[o + i] = r4[i];
     }
   }
 }
@@ -586,56 +677,96 @@ int32_t launch_status(const char* what) {
   return pkv::ok();
 }
 
-// Default partition: enough (sequence, kv head, partition) workgroups to
-// fill the chip several times over (about 2048), in power-of-two token
-// counts between 256 and 2048.  The upper bound keeps one workgroup's share
-// of a long context short enough that a batch of mixed lengths does not end
-// on a few long workgroups; the 32k layer measures best at 2048.
-constexpr int64_t kTargetWorkgroups = 2048;
-constexpr int32_t kMinPartition = 256;
-constexpr int32_t kMaxPartition = 2048;
+// Workgroups per kv head.  partition_size == 0: one round of resident
+// workgroups (compute units x occupancy, at most kMaxOcc per unit) spread
+// over the kv heads; partition_size > 0: about partition_size tokens per
+// workgroup for a batch of num_seqs x max_context_len tokens.
+constexpr int kMaxOcc = 8;
+constexpr int64_t kMaxWgsPerHead = 1 << 20;
 
-int32_t default_partition(int64_t num_seqs, int64_t num_kv_heads, int64_t max_context_len, int32_t block_size) {
-  const int64_t pairs = num_seqs * num_kv_heads > 0 ? num_seqs * num_kv_heads : 1;
-  const int64_t parts = (kTargetWorkgroups + pairs - 1) / pairs;
-  const int64_t want = (max_context_len + parts - 1) / parts;
-  int32_t P = kMinPartition;
-  while (P < kMaxPartition && P < want) P *= 2;
-  return P < block_size ? block_size : P;
+int64_t wgs_per_head_for(int64_t num_seqs, int64_t num_kv_heads, int64_t max_context_len, int32_t partition_size,
+                         int64_t cus, int64_t occ) {
+  int64_t n;
+  if (partition_size == 0) {
+    const int64_t slots = cus * (occ < kMaxOcc ? occ : kMaxOcc);
+    n = slots / num_kv_heads;
+  } else {
+    n = (num_seqs * max_context_len + partition_size - 1) / partition_size;
+  }
+  if (n < 1) n = 1;
+  if (n > kMaxWgsPerHead) n = kMaxWgsPerHead;
+  return n;
 }
 
-int32_t resolve_partition(int32_t partition_size, int32_t block_size, int64_t num_seqs, int64_t num_kv_heads,
-                          int64_t max_context_len, int32_t* out) {
-  int32_t P = partition_size == 0 ? default_partition(num_seqs, num_kv_heads, max_context_len, block_size)
-                                  : partition_size;
-  if (P <= 0 || P % block_size)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "partition_size %d must be a positive multiple of block_size %d", P,
-                     block_size);
-  *out = P;
-  return PKV_OK;
+// Workspace: 256-byte aligned regions
+//   meta int32[S*Hkv*2] | m float[N*2*G] | l float[N*2*G] | acc float[N*2*G*D]
+struct WsLayout {
+  int64_t meta, m, l, acc, total;
+};
+
+inline int64_t align256(int64_t x) { return ((x + 255) / 256) * 256; }
+
+WsLayout ws_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t group, int64_t head_dim, int64_t nwg) {
+  WsLayout w;
+  const int64_t rows = nwg * 2 * group;
+  w.meta = 0;
+  w.m = w.meta + align256(4 * num_seqs * num_kv_heads * 2);
+  w.l = w.m + align256(4 * rows);
+  w.acc = w.l + align256(4 * rows);
+  w.total = w.acc + align256(4 * rows * head_dim);
+  return w;
 }
 
-size_t workspace_for(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t max_parts) {
-  if (max_parts <= 1) return 0;
-  const int64_t rows = num_seqs * num_q_heads * max_parts;
-  const int64_t acc = ((rows * head_dim * 4 + 255) / 256) * 256;
-  const int64_t ml = ((rows * 4 + 255) / 256) * 256;
-  return static_cast<size_t>(acc + 2 * ml);
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Resident workgroups per compute unit of one decode instantiation (cached).
+template <bool BF16, int D, int BS>
+int decode_occupancy() {
+  static std::atomic<int> occ{0};
+  int v = occ.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<BF16, D, BS>, kThreads, 0) != hipSuccess || n <= 0)
+    n = 1;
+  occ.store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int occupancy_for(pkv_dtype dt, int32_t head_dim, int32_t block_size) {
+  if (dt == PKV_BF16) {
+    if (head_dim == 128) return block_size == 16 ? decode_occupancy<true, 128, 16>() : decode_occupancy<true, 128, 32>();
+    return block_size == 16 ? decode_occupancy<true, 64, 16>() : decode_occupancy<true, 64, 32>();
+  }
+  if (head_dim == 128) return block_size == 16 ? decode_occupancy<false, 128, 16>() : decode_occupancy<false, 128, 32>();
+  return block_size == 16 ? decode_occupancy<false, 64, 16>() : decode_occupancy<false, 64, 32>();
 }
 
 template <bool BF16, int D, int BS>
-void launch_decode(const DecodeArgs& a, int32_t num_seqs, hipStream_t st) {
-  dim3 grid(a.max_parts, a.num_kv_heads, num_seqs);
-  decode_partition_kernel<BF16, D, BS><<<grid, kThreads, 0, st>>>(a);
-  if (a.max_parts > 1) decode_merge_kernel<BF16, D><<<dim3(a.num_kv_heads, num_seqs), kThreads, 0, st>>>(a);
+void launch_decode(const DecodeArgs& a, hipStream_t st) {
+  const uint32_t nwg = static_cast<uint32_t>(static_cast<int64_t>(a.wgs_per_head) * a.num_kv_heads);
+  decode_kernel<BF16, D, BS><<<dim3(nwg), kThreads, 0, st>>>(a);
+  decode_merge_kernel<BF16, D><<<dim3(a.num_kv_heads, a.num_seqs), kThreads, 0, st>>>(a);
 }
 
 template <bool BF16, int D>
-void dispatch_bs(const DecodeArgs& a, int32_t num_seqs, int32_t bs, hipStream_t st) {
+void dispatch_bs(const DecodeArgs& a, int32_t bs, hipStream_t st) {
   if (bs == 16)
-    launch_decode<BF16, D, 16>(a, num_seqs, st);
+    launch_decode<BF16, D, 16>(a, st);
   else
-    launch_decode<BF16, D, 32>(a, num_seqs, st);
+    launch_decode<BF16, D, 32>(a, st);
 }
 
 }  // namespace
@@ -699,29 +830,33 @@ int32_t paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ds
   return launch_status("paged_kv_copy_blocks");
 }
 
-int32_t paged_attention_default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                          int32_t block_size, int32_t max_context_len) {
-  if (int32_t e = check_common(head_dim, block_size, PKV_BF16)) return e;
-  if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0)
+int32_t paged_attention_workgroups_per_head(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t block_size, int32_t max_context_len, int32_t partition_size,
+                                            pkv_dtype dt) {
+  if (int32_t e = check_common(head_dim, block_size, dt)) return e;
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || partition_size < 0)
     return pkv::fail(PKV_ERR_INVALID_ARG, "bad sizes");
-  int32_t P = 0;
-  if (int32_t e = resolve_partition(0, block_size, num_seqs, num_kv_heads, max_context_len, &P)) return e;
+  const int64_t n = wgs_per_head_for(num_seqs, num_kv_heads, max_context_len, partition_size, device_cus(),
+                                     occupancy_for(dt, head_dim, block_size));
   pkv::ok();
-  return P;
+  return static_cast<int32_t>(n);
 }
 
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                        int32_t block_size, int32_t max_context_len, int32_t partition_size) {
   if (check_common(head_dim, block_size, PKV_BF16)) return 0;
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 || partition_size < 0 ||
+      num_q_heads % num_kv_heads) {
     pkv::fail(PKV_ERR_INVALID_ARG, "bad sizes");
     return 0;
   }
-  int32_t P = 0;
-  if (resolve_partition(partition_size, block_size, num_seqs, num_kv_heads, max_context_len, &P)) return 0;
-  const int64_t max_parts = (static_cast<int64_t>(max_context_len) + P - 1) / P;
   pkv::ok();
-  return workspace_for(num_seqs, num_q_heads, head_dim, max_parts);
+  if (num_seqs == 0) return 0;
+  // Sized for the largest occupancy the launch may use, so the size does not
+  // depend on the element type.
+  const int64_t n = wgs_per_head_for(num_seqs, num_kv_heads, max_context_len, partition_size, device_cus(), kMaxOcc);
+  return static_cast<size_t>(ws_layout(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim,
+                                       n * num_kv_heads).total);
 }
 
 int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -753,18 +888,18 @@ int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, co
     return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return pkv::fail(PKV_ERR_INVALID_ARG, "q, out and the pools must be 16-byte aligned");
-  int32_t P = 0;
-  if (int32_t e = resolve_partition(partition_size, block_size, num_seqs, num_kv_heads, max_context_len, &P))
-    return e;
-  const int64_t max_parts = max_context_len == 0 ? 1 : (static_cast<int64_t>(max_context_len) + P - 1) / P;
-  if (max_parts > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "too many partitions");
-  const size_t need = workspace_for(num_seqs, num_q_heads, head_dim, max_parts);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return pkv::fail(PKV_ERR_CAPACITY, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return pkv::fail(PKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  }
+  if (partition_size < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "partition_size %d < 0", partition_size);
+  if (static_cast<int64_t>(num_seqs) * max_blocks_per_seq > INT32_MAX)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_seqs * max_blocks_per_seq exceeds the int32 range");
+  const int64_t wph = wgs_per_head_for(num_seqs, num_kv_heads, max_context_len, partition_size, device_cus(),
+                                       occupancy_for(dt, head_dim, block_size));
+  if (wph * num_kv_heads > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "too many workgroups");
+  const WsLayout wl = ws_layout(num_seqs, num_kv_heads, G, head_dim, wph * num_kv_heads);
+  const size_t need = static_cast<size_t>(wl.total);
+  if (!workspace || workspace_bytes < need)
+    return pkv::fail(PKV_ERR_CAPACITY, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   DecodeArgs a;
   a.out = out;
   a.q = q;
@@ -772,33 +907,31 @@ int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, co
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * max_parts;
   char* ws = static_cast<char*>(workspace);
-  const int64_t acc_bytes = ((rows * head_dim * 4 + 255) / 256) * 256;
-  const int64_t ml_bytes = ((rows * 4 + 255) / 256) * 256;
-  a.ws_acc = need ? reinterpret_cast<float*>(ws) : nullptr;
-  a.ws_m = need ? reinterpret_cast<float*>(ws + acc_bytes) : nullptr;
-  a.ws_l = need ? reinterpret_cast<float*>(ws + acc_bytes + ml_bytes) : nullptr;
+  a.meta = reinterpret_cast<int32_t*>(ws + wl.meta);
+  a.ws_m = reinterpret_cast<float*>(ws + wl.m);
+  a.ws_l = reinterpret_cast<float*>(ws + wl.l);
+  a.ws_acc = reinterpret_cast<float*>(ws + wl.acc);
+  a.wgs_per_head = static_cast<int32_t>(wph);
+  a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = G;
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
-  a.partition_size = P;
-  a.max_parts = static_cast<int32_t>(max_parts);
   a.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dt == PKV_BF16) {
     if (head_dim == 128)
-      dispatch_bs<true, 128>(a, num_seqs, block_size, st);
+      dispatch_bs<true, 128>(a, block_size, st);
     else
-      dispatch_bs<true, 64>(a, num_seqs, block_size, st);
+      dispatch_bs<true, 64>(a, block_size, st);
   } else {
     if (head_dim == 128)
-      dispatch_bs<false, 128>(a, num_seqs, block_size, st);
+      dispatch_bs<false, 128>(a, block_size, st);
     else
-      dispatch_bs<false, 64>(a, num_seqs, block_size, st);
+      dispatch_bs<false, 64>(a, block_size, st);
   }
   return launch_status("paged_attention_decode");
 }

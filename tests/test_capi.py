@@ -64,7 +64,7 @@ def test_host_validation_rejects_before_any_device_call():
     assert call(Hq=9) == N.PKV_ERR_INVALID_ARG  # not a multiple of Hkv
     assert call(Hq=32, Hkv=2) == N.PKV_ERR_UNSUPPORTED  # G = 16 > 8 for bf16
     assert call(ml=65) == N.PKV_ERR_INVALID_ARG  # beyond max_blocks * bs
-    assert call(P=24) == N.PKV_ERR_INVALID_ARG  # not a multiple of bs
+    assert call(P=-16) == N.PKV_ERR_INVALID_ARG  # negative partition size
     assert call(scale=float("nan")) == N.PKV_ERR_INVALID_ARG
     assert call(S=0) == 0
     assert call() == N.PKV_ERR_INVALID_ARG  # null pointers
@@ -73,10 +73,15 @@ def test_host_validation_rejects_before_any_device_call():
 def test_workspace_size_formula():
     import paged_kv_cache_230_amd as p
 
-    # one partition -> no workspace
-    assert p.paged_attention_workspace_bytes(4, 8, 2, 128, 16, 1024, 1024) == 0
-    # S*Hq*parts rows of D floats (+ m and l), each region 256-byte aligned
-    n = p.paged_attention_workspace_bytes(16, 64, 8, 128, 16, 32768, 512)
-    rows = 16 * 64 * 64
-    assert n == rows * 128 * 4 + 2 * rows * 4
-    assert p.paged_attention_default_partition(16, 8, 128, 16, 32768) % 16 == 0
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    def expect(S, Hq, Hkv, D, wph):
+        rows = wph * Hkv * 2 * (Hq // Hkv)
+        return a256(4 * S * Hkv * 2) + 2 * a256(4 * rows) + a256(4 * rows * D)
+
+    assert p.paged_attention_workspace_bytes(0, 8, 2, 128, 16, 1024, 1024) == 0
+    # partition_size > 0: about S*max_len/partition_size workgroups per kv head
+    assert p.paged_attention_workspace_bytes(4, 8, 2, 128, 16, 1024, 1024) == expect(4, 8, 2, 128, 4)
+    assert p.paged_attention_workspace_bytes(16, 64, 8, 128, 16, 32768, 512) == expect(16, 64, 8, 128, 1024)
+    assert p.paged_attention_workspace_bytes(3, 8, 2, 128, 16, 100, 10 ** 6) == expect(3, 8, 2, 128, 1)

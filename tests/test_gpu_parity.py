@@ -115,8 +115,9 @@ def test_split_matches_unsplit_fp32():
 
     out_one = torch.empty_like(out_split)
     q = w.q(0).cuda()
+    # partition_size >= num_seqs * max_len: one workgroup per kv head, nothing split
     paged_attention_decode(out_one, q, cache.k_cache, cache.v_cache, tables, lens, int(lh.max()),
-                           partition_size=int(lh.max() + 15) // 16 * 16)
+                           partition_size=len(lh) * int(lh.max()))
     paged_attention_decode(out_split, q, cache.k_cache, cache.v_cache, tables, lens, int(lh.max()),
                            partition_size=256)
     torch.cuda.synchronize()
