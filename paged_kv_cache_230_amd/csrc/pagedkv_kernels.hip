@@ -47,6 +47,11 @@ typedef __attribute__((ext_vector_type(4))) float float4v;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+// Block ids of a segment are staged in LDS this many at a time, so the step
+// loop reads them with LDS loads (ordered by lgkmcnt) rather than vector
+// memory loads, whose in-order completion counter would make each table read
+// wait for the K/V loads still in flight.
+constexpr int kIdChunk = 1024;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
@@ -188,6 +193,7 @@ struct DecodeSmem {
   int wave_sum[kWaves];
   int found_seq;
   int found_pre;
+  int ids[kIdChunk];  // block ids of the current chunk of the segment
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
@@ -268,9 +274,9 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
   const char* vbase = static_cast<const char*>(a.v_cache);
   constexpr size_t EB = BF16 ? 2 : 4;
 
-  auto tile_ptrs = [&](int j, const void*& kt, const void*& vt) {
-    int b = tbl[j];
-    if (static_cast<unsigned>(b) >= static_cast<unsigned>(a.num_blocks)) b = 0;
+  // Tile pointers of chunk-local block c (block id from LDS, made scalar).
+  auto tile_ptrs = [&](int c, const void*& kt, const void*& vt) {
+    const int b = __builtin_amdgcn_readfirstlane(sm.ids[c]);
     const size_t off = (static_cast<size_t>(b) * block_stride + head_off) * EB;
     kt = kbase + off;
     vt = vbase + off;
@@ -282,38 +288,16 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  constexpr int HALVES = BS / 16;
-  Step<BF16, D> cur[HALVES], nxt[HALVES];
-
-  int j = w;
-  if (j < nblk) {
-    const void *kt, *vt;
-    tile_ptrs(j, kt, vt);
-#pragma unroll
-    for (int h = 0; h < HALVES; ++h) load_step<BF16, D, BS>(cur[h], kt, vt, h, row, quad);
-  }
-  for (; j < nblk; j += kWaves) {
-    const int jn = j + kWaves;
-    if (jn < nblk) {
-      const void *kt, *vt;
-      tile_ptrs(jn, kt, vt);
-#pragma unroll
-      for (int h = 0; h < HALVES; ++h) load_step<BF16, D, BS>(nxt[h], kt, vt, h, row, quad);
-    }
-#pragma unroll
-    for (int h = 0; h < HALVES; ++h) {
-      const int tok_base = start + j * BS + 16 * h;
-      if (tok_base >= end) break;  // wave-uniform: the rest of the block is past the context
-      Step<BF16, D>& st = cur[h];
+  auto compute_step = [&](Step<BF16, D>& st, const int tok_base) {
 
       // Scores S[token 4*quad+i][head row] for the 16 tokens of this step.
       float4v sc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (BF16) {
-#pragma unroll
+  #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
           sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st.k[kk]), qo.q[kk], sc, 0, 0, 0);
       } else {
-#pragma unroll
+  #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
           sc = __builtin_amdgcn_mfma_f32_16x16x4f32(st.k[kk].x, qo.q[kk].x, sc, 0, 0, 0);
           sc = __builtin_amdgcn_mfma_f32_16x16x4f32(st.k[kk].y, qo.q[kk].y, sc, 0, 0, 0);
@@ -324,10 +308,10 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
       const bool tail = tok_base + 16 > end;  // wave-uniform
       const int tok0 = tok_base + 4 * quad;
       float x[4];
-#pragma unroll
+  #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = sc[i] * a.scale_log2;
       if (tail) {
-#pragma unroll
+  #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (tok0 + i >= end) x[i] = -INFINITY;
         mask_v<BF16, D>(st, tok0, end);
@@ -338,28 +322,28 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
       const float m_new = fmaxf(m_run, bmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       float pr[4];
-#pragma unroll
+  #pragma unroll
       for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
       l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
       if (__any(m_new > m_run)) {
         // Accumulator row r = 4*quad + v holds head (r mod 8) for bf16 (rows
         // 8..15 carry the low parts), head r for fp32; fetch its alpha.
         float av[4];
-#pragma unroll
+  #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int src = BF16 ? ((4 * quad + v) & 7) : (4 * quad + v);
           av[v] = __shfl(alpha, src, 64);
         }
-#pragma unroll
+  #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
+  #pragma unroll
           for (int v = 0; v < 4; ++v) acc.o[nt][v] *= av[v];
       }
       m_run = m_new;
 
       if constexpr (BF16) {
         short4v pa;
-#pragma unroll
+  #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float other = row_rotate8(pr[i]);  // lanes 8..15 receive heads 0..7
           uint16_t bits;
@@ -371,12 +355,12 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
           }
           pa[i] = static_cast<short>(bits);
         }
-#pragma unroll
+  #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           acc.o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(short4v, st.v[nt]), acc.o[nt],
                                                                 0, 0, 0);
       } else {
-#pragma unroll
+  #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           acc.o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[0], st.v[nt].x, acc.o[nt], 0, 0, 0);
           acc.o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[1], st.v[nt].y, acc.o[nt], 0, 0, 0);
@@ -384,9 +368,53 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
           acc.o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[3], st.v[nt].w, acc.o[nt], 0, 0, 0);
         }
       }
+  };
+
+  // The wave walks its blocks j = w, w + 4, ... in steps of 16 tokens (two
+  // steps per block when BS = 32), loading step n+1 while computing step n.
+  // Block ids come through LDS, kIdChunk at a time.
+  constexpr int HALVES = BS / 16;
+  for (int c0 = 0; c0 < nblk; c0 += kIdChunk) {
+    const int cn = nblk - c0 < kIdChunk ? nblk - c0 : kIdChunk;
+    for (int i = threadIdx.x; i < cn; i += kThreads) {
+      const int b = tbl[c0 + i];
+      sm.ids[i] = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks) ? b : 0;
     }
-#pragma unroll
-    for (int h = 0; h < HALVES; ++h) cur[h] = nxt[h];
+    __syncthreads();
+    Step<BF16, D> st, nxt;
+    const void* kt = nullptr;
+    const void* vt = nullptr;
+    int j = c0 + w;
+    int h = 0;
+    const int jend = c0 + cn;
+    if (j < jend) {
+      tile_ptrs(j - c0, kt, vt);
+      load_step<BF16, D, BS>(st, kt, vt, 0, row, quad);
+      // Every loop trip issues the next step's loads unconditionally, so the
+      // wait before the current step's math covers only its own loads; the
+      // last step runs after the loop.
+      for (;;) {
+        int jn = j;
+        int hn = h + 1;
+        const void* ktn = kt;
+        const void* vtn = vt;
+        if (hn == HALVES || start + j * BS + 16 * hn >= end) {  // wave-uniform
+          hn = 0;
+          jn = j + kWaves;
+        }
+        if (jn >= jend) break;
+        if (hn == 0) tile_ptrs(jn - c0, ktn, vtn);
+        load_step<BF16, D, BS>(nxt, ktn, vtn, hn, row, quad);
+        compute_step(st, start + j * BS + 16 * h);
+        st = nxt;
+        j = jn;
+        h = hn;
+        kt = ktn;
+        vt = vtn;
+      }
+      compute_step(st, start + j * BS + 16 * h);
+    }
+    __syncthreads();  // sm.ids is rewritten by the next chunk
   }
 
   // Per-wave totals: l over the four lane rows; bf16 high + low accumulator rows.
@@ -454,8 +482,13 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
 // the workgroup holding the sequence's first block records (first
 // workgroup, number of pieces) for the merge kernel.  With 8 kv heads the
 // round-robin dealing of workgroups to the 8 XCDs gives each XCD one head.
+// Minimum waves per SIMD the compiler must leave room for: 3 for bf16 (142
+// VGPRs at head_dim 128, no spills); fp32 keeps its natural allocation.
+template <bool BF16>
+constexpr int kDecodeMinWaves = BF16 ? 3 : 1;
+
 template <bool BF16, int D, int BS>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<BF16, D> sm;
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
