@@ -2,10 +2,11 @@
 """Decode-step benchmark of the paged KV-cache hot path on one MI355X.
 
 One step = the whole hot path over one batch: host bookkeeping (slot and
-copy-on-write reservation in the block manager, block-table export), the
-host-to-device copy of the tables, the copy-on-write block copy (when any),
-the cache append of one token per sequence, and split-context decode
-attention with its log-sum-exp merge.  Consecutive steps are real decode
+copy-on-write reservation in the block manager) staged to the GPU with
+pkv_bm_stage_step (one kernel reads the step's record from pinned memory
+and updates the device-resident block tables, lengths, slots and copy
+pairs), the copy-on-write block copy (when any), the cache append of one
+token per sequence, and decode attention with its log-sum-exp merge.  Consecutive steps are real decode
 steps: every sequence grows by one token per step, new blocks are taken at
 block boundaries.
 
@@ -176,59 +177,44 @@ def main():
     lens_d = torch.empty(S, dtype=torch.int32, device=dev)
     slots_d = torch.empty(S, dtype=torch.int32, device=dev)
     pairs_d = torch.empty(S, 2, dtype=torch.int32, device=dev)
+    # Two pinned step records, alternated.  A record is rewritten only after
+    # the GPU has read it: the decode-end event of the step that used it
+    # (recorded after that step's staging kernel) has completed.  No extra
+    # event is recorded for this, since every marker costs a dispatch gap.
     RING = 2
-    tables_h = [torch.empty(S, max_blocks, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
-    lens_h = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
-    slots_h = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
-    pairs_h = [torch.empty(S, 2, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
-    h2d_done = [torch.cuda.Event() for _ in range(RING)]
-    for e in h2d_done:
-        e.record()
-    ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
+    stage_cap = pkv.BlockManager.stage_capacity(S, max_blocks)
+    stage = [torch.zeros(stage_cap, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
     ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
     host_s = [0.0] * nsteps
-    seg = {"sync": 0.0, "bookkeeping": 0.0, "h2d": 0.0, "append": 0.0, "decode": 0.0}
+    seg = {"wait": 0.0, "bookkeeping+stage": 0.0, "copy+append": 0.0, "decode": 0.0}
     step_lens = []
-    n_cow = 0
+    n_cow_total = 0
 
     def step(k):
-        nonlocal n_cow
+        nonlocal n_cow_total
         th = time.perf_counter()
         r = k % RING
-        h2d_done[r].synchronize()  # the copies that last read ring slot r are done
-        ev_start[k].record()
+        if k >= RING:
+            ev1[k - RING].synchronize()  # the GPU has read record r
         t1 = time.perf_counter()
-        slots, pairs = bm.append_slots(seqs)
-        tnp, lnp = tables_h[r].numpy(), lens_h[r].numpy()
-        bm.block_tables(seqs, max_blocks, tnp, lnp)
-        slots_h[r].numpy()[:] = slots
-        npairs = pairs.shape[0]
-        if npairs:
-            pairs_h[r].numpy()[:npairs] = pairs
-            n_cow += npairs
-        step_lens.append(lnp.copy())
+        n_cow, max_len = bm.stage_step(seqs, stage[r], tables_d, lens_d, slots_d, pairs_d)
+        step_lens.append(stage[r].numpy()[4 + S: 4 + 2 * S].copy())  # lengths in the record
         t2 = time.perf_counter()
-        tables_d.copy_(tables_h[r], non_blocking=True)
-        lens_d.copy_(lens_h[r], non_blocking=True)
-        slots_d.copy_(slots_h[r], non_blocking=True)
-        if npairs:
-            pairs_d[:npairs].copy_(pairs_h[r][:npairs], non_blocking=True)
-        h2d_done[r].record()
-        t3 = time.perf_counter()
-        if npairs:
-            pkv.paged_kv_copy_blocks(cache.k_cache, cache.v_cache, pairs_d[:npairs])
+        if n_cow:
+            pkv.paged_kv_copy_blocks(cache.k_cache, cache.v_cache, pairs_d[:n_cow])
+            n_cow_total += n_cow
         pkv.paged_kv_append(step_k[k], step_v[k], cache.k_cache, cache.v_cache, slots_d)
+        t3 = time.perf_counter()
         ev0[k].record()
-        t4 = time.perf_counter()
-        pkv.paged_attention_decode(out, step_q[k], cache.k_cache, cache.v_cache, tables_d, lens_d,
-                                   int(lnp.max()), partition_size=P, workspace=workspace)
+        pkv.paged_attention_decode(out, step_q[k], cache.k_cache, cache.v_cache, tables_d, lens_d, max_len,
+                                   partition_size=P, workspace=workspace)
         ev1[k].record()
-        t5 = time.perf_counter()
-        host_s[k] = t5 - th
+        t4 = time.perf_counter()
+        host_s[k] = t4 - th
         if k >= args.warmup:
-            for name, dt in (("sync", t1 - th), ("bookkeeping", t2 - t1), ("h2d", t3 - t2), ("append", t4 - t3),
-                             ("decode", t5 - t4)):
+            for name, dt in (("wait", t1 - th), ("bookkeeping+stage", t2 - t1), ("copy+append", t3 - t2),
+                             ("decode", t4 - t3)):
                 seg[name] += dt
 
     if args.calibrate_copy:
@@ -293,9 +279,8 @@ def main():
         "decode_call_us": round(mean_dec_s * 1e6, 2),
         "decode_kv_gbps": round((sum(kv_bytes) / len(kv_bytes)) / mean_dec_s / 1e9, 2),
         "decode_tflops": round((sum(flops) / len(flops)) / mean_dec_s / 1e12, 2),
-        "cow_pairs": n_cow,
+        "cow_pairs": n_cow_total,
         "host_us_per_step": round(1e6 * sum(host_s[k] for k in timed) / args.steps, 1),
-        "gpu_step_us": round(1e3 * sum(ev_start[k].elapsed_time(ev1[k]) for k in timed) / args.steps, 1),
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_attention_decode (partition kernel + log-sum-exp merge)",

@@ -229,6 +229,37 @@ int32_t pkv_bm_free_seq(pkv_block_manager* bm, int64_t seq_id);
 int32_t pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs,
                             int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out);
 
+/* One decode step's host side without host-to-device copies.  Reserves   */
+/* one slot per sequence (as pkv_bm_append_slots with one token each),    */
+/* then writes a compact record into `stage` and launches, on `stream`, a */
+/* small kernel that reads the record in place (over the bus) and         */
+/* updates the device buffers:                                            */
+/*   slot_mapping [n_seqs], context_lens [n_seqs] (after the append),     */
+/*   cow_pairs [n][2] (the copies to run before writing the tokens),      */
+/*   block_tables [n_seqs][max_blocks_per_seq]: only the entries that     */
+/*   changed since the last call on the same table are written (new       */
+/*   blocks, copy-on-write replacements, sequences that moved rows); the  */
+/*   first call on a table, a different table or width, or full != 0     */
+/*   writes every used entry.  Entries past ceil(L / bs) are not written. */
+/* The table must only be written by this function between calls.        */
+/* stage         : pinned host memory (hipHostMalloc / pinned tensor) of  */
+/*                 stage_capacity int32, at least                         */
+/*                 pkv_bm_stage_capacity(n_seqs, max_blocks_per_seq); the */
+/*                 GPU reads it after this call returns, so it must not   */
+/*                 be rewritten until that kernel has run (alternate two  */
+/*                 buffers and wait on an event)                          */
+/* cow_pairs     : device, room for n_seqs pairs                          */
+/* *n_cow_out    : pairs written; *max_len_out: largest context length    */
+/* All device buffers are int32.  Errors before the reservation leave the */
+/* manager unchanged.                                                     */
+int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs, int32_t* stage,
+                          int32_t stage_capacity, int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t* context_lens, int32_t* slot_mapping, int32_t* cow_pairs, int32_t cow_capacity,
+                          int32_t full, int32_t* n_cow_out, int32_t* max_len_out, void* stream);
+
+/* Worst-case stage size (int32 count) for pkv_bm_stage_step.              */
+int32_t pkv_bm_stage_capacity(int32_t n_seqs, int32_t max_blocks_per_seq);
+
 /* Queries.  Negative status on a bad handle or id.                        */
 int32_t pkv_bm_num_free(const pkv_block_manager* bm);
 int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);

@@ -80,6 +80,9 @@ _SIGS = {
     "pkv_bm_seq_len": (_i32, [_vp, _i64]),
     "pkv_bm_num_seqs": (_i32, [_vp]),
     "pkv_bm_free_stack": (_i32, [_vp, _pi32, _i32]),
+    "pkv_bm_stage_step": (
+        _i32, [_vp, _pi64, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _pi32, _pi32, _vp]),
+    "pkv_bm_stage_capacity": (_i32, [_i32, _i32]),
 }
 
 for _name, (_res, _args) in _SIGS.items():

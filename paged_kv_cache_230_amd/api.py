@@ -243,6 +243,43 @@ class BlockManager:
                                           _i32p(lens_out)))
         return tables_out, lens_out
 
+    def stage_step(self, seq_ids, stage, block_tables, context_lens, slot_mapping, cow_pairs, full=False):
+        """One decode step's bookkeeping, staged to the device without copies.
+
+        ``stage``: pinned int32 CPU tensor of at least ``stage_capacity``
+        entries (alternate two and wait for the GPU before reusing one);
+        ``block_tables`` [n][max_blocks], ``context_lens`` [n],
+        ``slot_mapping`` [n], ``cow_pairs`` [n][2]: int32 device tensors.
+        Returns ``(n_cow, max_len)``; the work runs on the current stream.
+        """
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        if not (stage.dtype == torch.int32 and stage.is_pinned() and stage.is_contiguous()):
+            raise ValueError("stage must be a contiguous pinned int32 CPU tensor")
+        dev = block_tables.device
+        for t, name, shape in ((block_tables, "block_tables", None), (context_lens, "context_lens", (n,)),
+                               (slot_mapping, "slot_mapping", (n,)), (cow_pairs, "cow_pairs", None)):
+            _need(t, name, torch.int32, dev)
+            if shape is not None and tuple(t.shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}")
+        if block_tables.dim() != 2 or block_tables.shape[0] != n:
+            raise ValueError("block_tables must be [n_seqs][max_blocks_per_seq]")
+        if cow_pairs.dim() != 2 or cow_pairs.shape[1] != 2:
+            raise ValueError("cow_pairs must be [capacity][2]")
+        n_cow, max_len = C.c_int32(0), C.c_int32(0)
+        N.check(
+            N.lib.pkv_bm_stage_step(
+                self._h, _i64p(ids), n, C.c_void_p(stage.data_ptr()), stage.numel(), _ptr(block_tables),
+                block_tables.shape[1], _ptr(context_lens), _ptr(slot_mapping), _ptr(cow_pairs), cow_pairs.shape[0],
+                int(bool(full)), C.byref(n_cow), C.byref(max_len), _stream(dev),
+            )
+        )
+        return n_cow.value, max_len.value
+
+    @staticmethod
+    def stage_capacity(n_seqs: int, max_blocks_per_seq: int) -> int:
+        return N.check(N.lib.pkv_bm_stage_capacity(int(n_seqs), int(max_blocks_per_seq)))
+
     def num_free(self) -> int:
         return N.check(N.lib.pkv_bm_num_free(self._h))
 

@@ -1,6 +1,6 @@
 """Build libpagedkv.so in-tree with hipcc for gfx950.
 
-``python -m paged_kv_cache_230_amd.build`` (or ``build()``) compiles the HIP
+``python paged_kv_cache_230_amd/build.py`` (or ``build()``) compiles the HIP
 kernels and the host block manager into one shared library next to this
 file.  The build always recompiles; the output is replaced atomically.
 """

@@ -32,12 +32,25 @@ struct pkv_block_manager {
   struct Seq {
     std::vector<int32_t> table;
     int32_t len = 0;
+    // Device mirror (pkv_bm_stage_step): row of the device table this
+    // sequence was last written to (-1: none), entries written there, and the
+    // lowest entry changed since (a copy-on-write replacement).
+    int32_t mirror_row = -1;
+    int32_t mirror_blocks = 0;
+    int32_t dirty_from = INT32_MAX;
   };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
   std::vector<int32_t> free_stack;  // back() is handed out next
   std::vector<int32_t> refcount;
   std::unordered_map<int64_t, Seq> seqs;
+  // Device table the mirror state refers to, and the sequence whose entries
+  // each of its rows last received.
+  const void* mirror_table = nullptr;
+  int32_t mirror_width = 0;
+  std::vector<int64_t> row_owner;
+  // Scratch reused by pkv_bm_stage_step.
+  std::vector<int32_t> scratch_slots, scratch_pairs;
 };
 
 namespace {
@@ -189,6 +202,7 @@ int32_t pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32
           bm->refcount[old] -= 1;
           bm->refcount[b] = 1;
           s.table[L / bs] = b;
+          if (L / bs < s.dirty_from) s.dirty_from = L / bs;
         }
       }
       slot_mapping_out[ns++] = s.table[L / bs] * bs + L % bs;
@@ -267,6 +281,118 @@ int32_t pkv_bm_free_stack(const pkv_block_manager* bm, int32_t* out, int32_t cap
   if (n > 0 && !out) return pkv::fail(PKV_ERR_INVALID_ARG, "out is null");
   std::copy(bm->free_stack.begin(), bm->free_stack.end(), out);
   return n;
+}
+
+
+int32_t pkv_bm_stage_capacity(int32_t n_seqs, int32_t max_blocks_per_seq) {
+  if (n_seqs < 0 || max_blocks_per_seq < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "negative size");
+  const int64_t need = 4 + 4 * static_cast<int64_t>(n_seqs) + 3 * static_cast<int64_t>(n_seqs) * max_blocks_per_seq;
+  if (need > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "stage size exceeds the int32 range");
+  pkv::ok();
+  return static_cast<int32_t>(need);
+}
+
+int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs, int32_t* stage,
+                          int32_t stage_capacity, int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t* context_lens, int32_t* slot_mapping, int32_t* cow_pairs, int32_t cow_capacity,
+                          int32_t full, int32_t* n_cow_out, int32_t* max_len_out, void* stream) {
+  if (int32_t e = check_handle(bm)) return e;
+  if (n_seqs < 0 || max_blocks_per_seq <= 0 || stage_capacity < 0 || cow_capacity < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (n_seqs == 0) {
+    if (n_cow_out) *n_cow_out = 0;
+    if (max_len_out) *max_len_out = 0;
+    return pkv::ok();
+  }
+  if (!seq_ids || !stage || !block_tables || !context_lens || !slot_mapping || !cow_pairs)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (cow_capacity < n_seqs)
+    return pkv::fail(PKV_ERR_CAPACITY, "copy-pair buffer holds %d pairs; one per sequence (%d) is required",
+                     cow_capacity, n_seqs);
+  const int32_t* stage_dev = nullptr;
+  if (int32_t e = pkv::stage_device_ptr(stage, &stage_dev)) return e;
+  const int32_t bs = bm->block_size;
+  const bool remap = full || bm->mirror_table != block_tables || bm->mirror_width != max_blocks_per_seq;
+
+  // Bound the record before anything changes, so every failure leaves the
+  // manager untouched (the append below validates ids and counts the rest).
+  int64_t bound = 4 + 4 * static_cast<int64_t>(n_seqs);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    const auto& q = it->second;
+    const bool owned = !remap && q.mirror_row == i && i < static_cast<int32_t>(bm->row_owner.size()) &&
+                       bm->row_owner[i] == seq_ids[i];
+    const int64_t nb_after = (static_cast<int64_t>(q.len) + 1 + bs - 1) / bs;
+    if (nb_after > max_blocks_per_seq)
+      return pkv::fail(PKV_ERR_CAPACITY, "sequence %lld would hold %lld blocks > max_blocks_per_seq %d",
+                       (long long)seq_ids[i], (long long)nb_after, max_blocks_per_seq);
+    int64_t from = 0;
+    if (owned) {
+      from = q.mirror_blocks;
+      if (q.dirty_from < from) from = q.dirty_from;
+      const int64_t write_at = q.len / bs;  // a copy-on-write may replace this entry
+      if (write_at < from) from = write_at;
+    }
+    bound += 3 * (nb_after - from);
+  }
+  if (bound > stage_capacity)
+    return pkv::fail(PKV_ERR_CAPACITY, "stage buffer holds %d ints, up to %lld needed", stage_capacity,
+                     (long long)bound);
+
+  bm->scratch_slots.resize(n_seqs);
+  bm->scratch_pairs.resize(2 * static_cast<size_t>(n_seqs));
+  int32_t ns = 0, nc = 0;
+  if (int32_t e = pkv_bm_append_slots(bm, seq_ids, n_seqs, nullptr, bm->scratch_slots.data(), n_seqs, &ns,
+                                      bm->scratch_pairs.data(), n_seqs, &nc))
+    return e;
+
+  // Record: [n, pairs, updates, width] slots[n] lens[n] pairs[2*pairs] updates[3*updates]
+  int32_t* slots = stage + 4;
+  int32_t* lens = slots + n_seqs;
+  int32_t* pairs = lens + n_seqs;
+  int32_t* upd = pairs + 2 * nc;
+  int32_t nu = 0, max_len = 0;
+  if (remap) bm->row_owner.clear();
+  if (static_cast<int32_t>(bm->row_owner.size()) < n_seqs) bm->row_owner.resize(n_seqs, -1);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto& q = bm->seqs.find(seq_ids[i])->second;
+    const bool owned = !remap && q.mirror_row == i && bm->row_owner[i] == seq_ids[i];
+    slots[i] = bm->scratch_slots[i];
+    lens[i] = q.len;
+    if (q.len > max_len) max_len = q.len;
+    const int32_t nb = static_cast<int32_t>(q.table.size());
+    int32_t from = 0;
+    if (owned) {
+      from = q.mirror_blocks < q.dirty_from ? q.mirror_blocks : q.dirty_from;
+      if (from > nb) from = nb;
+    }
+    for (int32_t c = from; c < nb; ++c) {
+      upd[3 * nu] = i;
+      upd[3 * nu + 1] = c;
+      upd[3 * nu + 2] = q.table[c];
+      ++nu;
+    }
+    q.mirror_row = i;
+    q.mirror_blocks = nb;
+    q.dirty_from = INT32_MAX;
+    bm->row_owner[i] = seq_ids[i];
+  }
+  for (int32_t k = 0; k < 2 * nc; ++k) pairs[k] = bm->scratch_pairs[k];
+  stage[0] = n_seqs;
+  stage[1] = nc;
+  stage[2] = nu;
+  stage[3] = max_blocks_per_seq;
+  if (remap) {
+    bm->mirror_table = block_tables;
+    bm->mirror_width = max_blocks_per_seq;
+  }
+  if (int32_t e = pkv::launch_stage(stage_dev, n_seqs, nc, nu, max_blocks_per_seq, slot_mapping, context_lens,
+                                    cow_pairs, block_tables, stream))
+    return e;
+  if (n_cow_out) *n_cow_out = nc;
+  if (max_len_out) *max_len_out = max_len;
+  return pkv::ok();
 }
 
 }  // extern "C"

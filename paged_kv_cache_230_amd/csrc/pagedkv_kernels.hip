@@ -692,6 +692,35 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_c
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) to[i] = from[i];
 }
 
+// Decode-step staging: copies the record written by pkv_bm_stage_step from
+// pinned host memory (read in place over the bus) into the device buffers:
+// slots, lengths, copy-on-write pairs, and the changed block-table entries.
+__global__ __launch_bounds__(256) void stage_kernel(const int32_t* __restrict__ stage, int32_t n, int32_t np,
+                                                   int32_t nu, int32_t width, int32_t* __restrict__ slots,
+                                                   int32_t* __restrict__ lens, int32_t* __restrict__ pairs,
+                                                   int32_t* __restrict__ tables) {
+  const int32_t* s_slots = stage + 4;
+  const int32_t* s_lens = s_slots + n;
+  const int32_t* s_pairs = s_lens + n;
+  const int32_t* s_upd = s_pairs + 2 * np;
+  const int64_t total = 2LL * n + 2LL * np + nu;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    if (i < n) {
+      slots[i] = s_slots[i];
+    } else if (i < 2LL * n) {
+      lens[i - n] = s_lens[i - n];
+    } else if (i < 2LL * n + 2LL * np) {
+      pairs[i - 2LL * n] = s_pairs[i - 2LL * n];
+    } else {
+      const int64_t u = i - 2LL * n - 2LL * np;
+      const int32_t row = s_upd[3 * u];
+      const int32_t col = s_upd[3 * u + 1];
+      if (row >= 0 && row < n && col >= 0 && col < width) tables[static_cast<int64_t>(row) * width + col] = s_upd[3 * u + 2];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 int32_t check_common(int32_t head_dim, int32_t block_size, pkv_dtype dt) {
   if (dt != PKV_F32 && dt != PKV_BF16) return pkv::fail(PKV_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
@@ -808,6 +837,42 @@ namespace pkv {
 std::string& last_error_slot() {
   thread_local std::string msg;
   return msg;
+}
+
+int32_t stage_device_ptr(const int32_t* stage, const int32_t** dev_out) {
+  // Cached for the last buffers seen (callers alternate a few stage buffers).
+  thread_local const void* host[4] = {nullptr, nullptr, nullptr, nullptr};
+  thread_local void* dev[4] = {nullptr, nullptr, nullptr, nullptr};
+  thread_local int next = 0;
+  for (int i = 0; i < 4; ++i)
+    if (host[i] == stage) {
+      *dev_out = static_cast<const int32_t*>(dev[i]);
+      return PKV_OK;
+    }
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<int32_t*>(stage), 0) != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_INVALID_ARG, "stage buffer is not pinned host memory (hipHostMalloc / pin_memory)");
+  }
+  host[next] = stage;
+  dev[next] = d;
+  next = (next + 1) & 3;
+  *dev_out = static_cast<const int32_t*>(d);
+  return PKV_OK;
+}
+
+int32_t launch_stage(const int32_t* stage_dev, int32_t n_seqs, int32_t n_pairs, int32_t n_updates, int32_t width,
+                     int32_t* slot_mapping, int32_t* context_lens, int32_t* cow_pairs, int32_t* block_tables,
+                     void* stream) {
+  const int64_t total = 2LL * n_seqs + 2LL * n_pairs + n_updates;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 1024) grid = 1024;
+  if (grid < 1) grid = 1;
+  stage_kernel<<<dim3(static_cast<uint32_t>(grid)), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      stage_dev, n_seqs, n_pairs, n_updates, width, slot_mapping, context_lens, cow_pairs, block_tables);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_DEVICE, "stage launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
 }
 }  // namespace pkv
 

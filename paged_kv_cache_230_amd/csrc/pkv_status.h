@@ -23,6 +23,16 @@ inline int32_t fail(int32_t code, const char* fmt, ...) {
   return code;
 }
 
+// Device address of a pinned host buffer (error if it is not pinned).
+int32_t stage_device_ptr(const int32_t* stage, const int32_t** dev);
+
+// Launches the staging kernel that copies one decode step's record from
+// pinned host memory (read in place by the GPU, at `stage_dev`) into the
+// device buffers.
+int32_t launch_stage(const int32_t* stage_dev, int32_t n_seqs, int32_t n_pairs, int32_t n_updates, int32_t width,
+                     int32_t* slot_mapping, int32_t* context_lens, int32_t* cow_pairs, int32_t* block_tables,
+                     void* stream);
+
 inline int32_t ok() {
   last_error_slot().clear();
   return PKV_OK;
