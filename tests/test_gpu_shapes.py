@@ -1,0 +1,96 @@
+"""Parity of every built kernel instantiation (dtype x head_dim x block_size)
+and of the group sizes the library accepts, on small seeded batches that
+still span several blocks, split ranges and a ragged tail."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import TOL, assert_close, say, storage_np
+
+import oracle.pool as opool
+import oracle.attention as oatt
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(dtype, d, bs, Hq, Hkv, lens, seed, partition_size, q_scale=None):
+    # fp32 follows the tiny fp32 configuration's N(0, 1) values, for which the
+    # 1e-5 bound is stated; bf16 scales q by 8 so the scores are not uniform.
+    if q_scale is None:
+        q_scale = 1.0 if dtype == "f32" else 8.0
+    import paged_kv_cache_230_amd as pkv
+
+    g = torch.Generator().manual_seed(seed)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    S = len(lens)
+    nblk = sum(-(-L // bs) for L in lens)
+    nb = nblk + 7
+    perm = torch.randperm(nb, generator=g).numpy()
+    maxb = max(1, max(-(-L // bs) for L in lens))
+    tables = np.full((S, maxb), -1, np.int32)
+    used = 0
+    slots = []
+    for s, L in enumerate(lens):
+        n = -(-L // bs)
+        tables[s, :n] = perm[used:used + n]
+        used += n
+        slots += [int(tables[s, t // bs]) * bs + t % bs for t in range(L)]
+    T = len(slots)
+    std = 1.0 if dtype == "f32" else 128 ** -0.5
+    kt = (torch.randn(T, Hkv, d, generator=g) * std).to(tdt)
+    vt = (torch.randn(T, Hkv, d, generator=g) * std).to(tdt)
+    q = (torch.randn(S, Hq, d, generator=g) * std * q_scale).to(tdt)
+    # product path
+    k_cache, v_cache = pkv.new_pools(nb, Hkv, d, bs, tdt)
+    sl = torch.tensor(slots, dtype=torch.int32)
+    if T:
+        pkv.paged_kv_append(kt.cuda(), vt.cuda(), k_cache, v_cache, sl.cuda())
+    out = torch.full((S, Hq, d), float("nan"), dtype=tdt, device="cuda")
+    pkv.paged_attention_decode(out, q.cuda(), k_cache, v_cache, torch.from_numpy(tables).cuda(),
+                               torch.tensor(lens, dtype=torch.int32).cuda(), max(lens), partition_size=partition_size)
+    torch.cuda.synchronize()
+    # oracle path
+    sd = np.float32 if dtype == "f32" else np.uint16
+    ok, ov = opool.new_pools(nb, Hkv, d, bs, sd)
+
+    def st(t):
+        return t.numpy() if t.dtype == torch.float32 else t.view(torch.int16).numpy().view(np.uint16)
+
+    opool.append(ok, ov, st(kt), st(vt), np.array(slots, np.int64))
+    ref = oatt.decode_attention(st(q), ok, ov, tables, np.array(lens))
+    assert np.array_equal(storage_np(k_cache).view(np.uint8), ok.view(np.uint8))
+    assert np.array_equal(storage_np(v_cache).view(np.uint8), ov.view(np.uint8))
+    return out, ref
+
+
+SHAPES = [(dt, d, bs) for dt in ("f32", "bf16") for d in (64, 128) for bs in (16, 32)]
+
+
+@pytest.mark.parametrize("dtype,d,bs", SHAPES, ids=[f"{a}-d{b}-bs{c}" for a, b, c in SHAPES])
+@pytest.mark.parametrize("part", [0, 48 * 32])
+def test_every_instantiation(dtype, d, bs, part):
+    lens = [1, bs - 1, bs, bs + 1, 7 * bs + 3, 40 * bs + 5, 3]
+    Hq, Hkv = 8, 2
+    say(f"case {dtype} d{d} bs{bs} partition {part}")
+    out, ref = _case(dtype, d, bs, Hq, Hkv, lens, seed=d + bs, partition_size=part)
+    assert_close(out, ref, dtype, f"{dtype} d{d} bs{bs} P{part}")
+
+
+GROUPS = [("f32", 1), ("f32", 3), ("f32", 16), ("bf16", 1), ("bf16", 5), ("bf16", 8)]
+
+
+@pytest.mark.parametrize("dtype,G", GROUPS, ids=[f"{a}-G{b}" for a, b in GROUPS])
+def test_group_sizes(dtype, G):
+    Hkv = 3
+    lens = [50, 333, 17, 129]
+    say(f"case {dtype} G={G}")
+    out, ref = _case(dtype, 128, 16, G * Hkv, Hkv, lens, seed=100 + G, partition_size=64)
+    assert_close(out, ref, dtype, f"{dtype} G{G}")
+
+
+def test_group_size_above_limit_is_rejected():
+    import paged_kv_cache_230_amd as pkv
+
+    with pytest.raises(pkv.PKVError) as e:
+        _case("bf16", 128, 16, 16 * 2, 2, [20], seed=1, partition_size=0)
+    assert "group size" in str(e.value)
