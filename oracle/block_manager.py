@@ -32,15 +32,69 @@ so the two can be compared bit for bit):
   (n may stop inside a block; the child's first write there copies it).
 * Every call is atomic: on any error nothing changes.
 
+Prefix caching by chained block digests ("PagedAttention et RadixAttention :
+parlons de KV Cache", the closing part on vLLM's automatic prefix caching and
+the paragraph on cache salting; "PagedAttention — Gestion mémoire pour LLM à
+long contexte", *Implications*: pages with identical token content may be
+shared between requests).  The pages fix that every completed block gets a
+digest of (its parent's digest, its own tokens, extra data), that equal token
+sequences therefore give equal chains and find the blocks already computed,
+and that a tenant-specific salt folded into the digest keeps equal requests
+of different tenants apart.  Readings where they are silent:
+
+* digest = SHA-256 of ``parent (32 bytes; zeros for block 0) || salt
+  (uint64, little-endian) || the block's token ids (int32, little-endian)``;
+  the salt is the extra data of every block;
+* a block is registered when it fills and every token id in it (and every
+  earlier block's digest) is known; if the digest is already registered to
+  another block the new block stays unregistered (a duplicate);
+* a lookup walks the prompt's full blocks from the first and stops at the
+  first digest that is not registered; matched blocks are shared as by fork;
+* a registered block whose reference count drops to zero is kept, with its
+  digest, on an eviction list (oldest first); a released sequence adds its
+  registered blocks from its last block to its first, so a chain's deeper
+  blocks are evicted before its head (least recently used leaves first,
+  shared heads last: same page, RadixAttention's eviction);
+* a new block comes from the free stack; only when that is empty is the
+  oldest evictable block taken, and its digest forgotten; a lookup hit on
+  an evictable block takes it off the list;
+* token ids are recorded only while they are given with every append; an
+  append without ids ends the sequence's chain (its later blocks are never
+  registered).
+
 Pins (``tests/test_oracle_block_manager.py``): after every operation the
 reference counts equal a from-scratch recount over all tables, free and
 used blocks partition the pool, every table has ``ceil(L/bs)`` entries;
 copy-on-write leaves the source block untouched; closed-form block counts
 for the shared-prefix workload; out-of-blocks leaves the state unchanged.
+Prefix cache (``tests/test_oracle_prefix_cache.py``): equal prompts share
+blocks, salts separate tenants, one changed token ends the match at its
+block, equal blocks at another depth miss, eviction order, the 50-request
+system-prompt saving in closed form, and a random run whose every lookup
+equals a brute force over token tuples (no hashing); planted mistakes in
+the digest or the eviction order fail these pins.
 """
 from __future__ import annotations
 
-__all__ = ["BlockManagerModel", "BMError", "OutOfBlocks", "UnknownSeq", "InvalidArg", "Capacity"]
+import hashlib
+
+__all__ = ["BlockManagerModel", "BMError", "OutOfBlocks", "UnknownSeq", "InvalidArg", "Capacity", "block_digest",
+           "ZERO_DIGEST"]
+
+ZERO_DIGEST = bytes(32)
+
+
+def block_digest(parent, salt, tokens):
+    """Chain digest of one full block: SHA-256(parent || salt || tokens)."""
+    if len(parent) != 32:
+        raise InvalidArg("parent digest must be 32 bytes")
+    if not 0 <= salt < 2 ** 64:
+        raise InvalidArg("salt must fit in 64 unsigned bits")
+    msg = bytearray(parent)
+    msg += int(salt).to_bytes(8, "little")
+    for t in tokens:
+        msg += int(t).to_bytes(4, "little", signed=True)
+    return hashlib.sha256(bytes(msg)).digest()
 
 
 class BMError(Exception):
@@ -80,13 +134,68 @@ class BlockManagerModel:
         self.refcount = [0] * num_blocks
         self.tables = {}
         self.lens = {}
+        # prefix cache
+        self.salt = {}
+        self.tokens = {}  # known leading token ids of each sequence
+        self.digests = {}  # chain digests of each sequence's leading full blocks
+        self.cached = {}  # digest -> registered block
+        self.block_digest = [None] * num_blocks
+        self.lru = []  # evictable registered blocks, oldest first
+
+    def _take(self):
+        if self.free:
+            return self.free.pop()
+        b = self.lru.pop(0)
+        del self.cached[self.block_digest[b]]
+        self.block_digest[b] = None
+        return b
+
+    def _available(self):
+        return len(self.free) + len(self.lru)
 
     # ------------------------------------------------------------ sequences
     def add_seq(self, sid):
+        self.add_seq_cached(sid, [], 0)
+
+    def _match(self, tokens, salt):
+        bs = self.block_size
+        blocks, digests = [], []
+        d = ZERO_DIGEST
+        for i in range(len(tokens) // bs):
+            d = block_digest(d, salt, tokens[i * bs:(i + 1) * bs])
+            b = self.cached.get(d)
+            if b is None:
+                break
+            blocks.append(b)
+            digests.append(d)
+        return blocks, digests
+
+    def match_prefix(self, tokens, salt=0):
+        """Prompt tokens a cached admission would share (a multiple of bs)."""
+        return len(self._match([int(t) for t in tokens], salt)[0]) * self.block_size
+
+    def add_seq_cached(self, sid, tokens, salt=0):
+        """Add a sequence for a prompt, sharing its registered leading blocks.
+
+        Returns the number of prompt tokens already cached; the sequence
+        starts at that length and the caller appends the rest."""
         if sid in self.tables:
             raise InvalidArg(f"sequence {sid} exists")
-        self.tables[sid] = []
-        self.lens[sid] = 0
+        if not 0 <= salt < 2 ** 64:
+            raise InvalidArg("salt must fit in 64 unsigned bits")
+        tokens = [int(t) for t in tokens]
+        blocks, digests = self._match(tokens, salt)
+        for b in blocks:
+            if self.refcount[b] == 0:
+                self.lru.remove(b)
+            self.refcount[b] += 1
+        n = len(blocks) * self.block_size
+        self.tables[sid] = list(blocks)
+        self.lens[sid] = n
+        self.salt[sid] = salt
+        self.tokens[sid] = tokens[:n]
+        self.digests[sid] = digests
+        return n
 
     def fork(self, parent, child, n):
         if parent not in self.tables:
@@ -100,16 +209,23 @@ class BlockManagerModel:
             self.refcount[b] += 1
         self.tables[child] = list(shared)
         self.lens[child] = n
+        self.salt[child] = self.salt[parent]
+        self.tokens[child] = self.tokens[parent][:n]
+        self.digests[child] = self.digests[parent][: n // self.block_size]
 
     def free_seq(self, sid):
         if sid not in self.tables:
             raise UnknownSeq(f"unknown sequence {sid}")
-        for b in self.tables[sid]:
+        table = self.tables[sid]
+        for b in table:
             self.refcount[b] -= 1
-            if self.refcount[b] == 0:
+            if self.refcount[b] == 0 and self.block_digest[b] is None:
                 self.free.append(b)
-        del self.tables[sid]
-        del self.lens[sid]
+        for b in reversed(table):
+            if self.refcount[b] == 0 and self.block_digest[b] is not None:
+                self.lru.append(b)
+        for m in (self.tables, self.lens, self.salt, self.tokens, self.digests):
+            del m[sid]
 
     # --------------------------------------------------------------- append
     def blocks_needed(self, sids, ntoks):
@@ -142,12 +258,13 @@ class BlockManagerModel:
                 dropped[last] = dropped.get(last, 0) + 1
         return n_cow
 
-    def append_slots(self, sids, ntoks=None, slot_capacity=None, cow_capacity=None):
+    def append_slots(self, sids, ntoks=None, slot_capacity=None, cow_capacity=None, token_ids=None):
         """Reserve slots for new tokens; returns ``(slots, cow_pairs)``.
 
         ``slots`` lists the slot of every new token, sequence-major in call
         order; ``cow_pairs`` lists ``(src, dst)`` block copies that must run
-        before the tokens are written.
+        before the tokens are written.  ``token_ids`` (same order as
+        ``slots``, or None) are the new tokens' ids, for the prefix cache.
         """
         sids = list(sids)
         ntoks = [1] * len(sids) if ntoks is None else [int(n) for n in ntoks]
@@ -161,33 +278,56 @@ class BlockManagerModel:
             if n < 0:
                 raise InvalidArg("negative token count")
         total = sum(ntoks)
+        if token_ids is not None:
+            token_ids = [int(t) for t in token_ids]
+            if len(token_ids) != total:
+                raise InvalidArg("one token id per new token")
         if slot_capacity is not None and total > slot_capacity:
             raise Capacity("slot buffer too small")
         if cow_capacity is not None and self.cow_needed(sids, ntoks) > cow_capacity:
             raise Capacity("copy-pair buffer too small")
-        if self.blocks_needed(sids, ntoks) > len(self.free):
+        if self.blocks_needed(sids, ntoks) > self._available():
             raise OutOfBlocks("not enough free blocks")
         bs = self.block_size
         slots, pairs = [], []
         for sid, n in zip(sids, ntoks):
             table = self.tables[sid]
+            known = self.tokens[sid]
             for _ in range(n):
                 L = self.lens[sid]
                 if L % bs == 0:
-                    b = self.free.pop()
+                    b = self._take()
                     self.refcount[b] = 1
                     table.append(b)
                 else:
                     old = table[L // bs]
                     if self.refcount[old] > 1:
-                        b = self.free.pop()
+                        b = self._take()
                         pairs.append((old, b))
                         self.refcount[old] -= 1
                         self.refcount[b] = 1
                         table[L // bs] = b
+                if token_ids is not None and len(known) == L:
+                    known.append(token_ids[len(slots)])
                 slots.append(table[L // bs] * bs + L % bs)
                 self.lens[sid] = L + 1
+                if (L + 1) % bs == 0:
+                    self._complete(sid, L // bs)
         return slots, pairs
+
+    def _complete(self, sid, i):
+        """Block i of sid just filled: give it its digest and register it."""
+        bs = self.block_size
+        known, digests = self.tokens[sid], self.digests[sid]
+        if len(known) < (i + 1) * bs or len(digests) != i:
+            return
+        parent = digests[i - 1] if i else ZERO_DIGEST
+        d = block_digest(parent, self.salt[sid], known[i * bs:(i + 1) * bs])
+        digests.append(d)
+        if d not in self.cached:
+            b = self.tables[sid][i]
+            self.cached[d] = b
+            self.block_digest[b] = d
 
     # ---------------------------------------------------------------- query
     def block_tables(self, sids, max_blocks):
@@ -203,7 +343,15 @@ class BlockManagerModel:
         return rows, lens
 
     def num_free(self):
-        return len(self.free)
+        """Blocks a new allocation can take: the free stack and the evictable list."""
+        return self._available()
+
+    def num_cached(self):
+        return len(self.cached)
+
+    def evictable(self):
+        """Evictable registered blocks, oldest (next evicted) first."""
+        return list(self.lru)
 
     def free_stack(self):
         """Free blocks, bottom to top (the next block handed out is last)."""
@@ -220,5 +368,27 @@ class BlockManagerModel:
         free = set(self.free)
         assert len(free) == len(self.free), "block twice in the free pool"
         used = {b for b in range(self.num_blocks) if recount[b] > 0}
-        assert not (free & used), "block both free and in use"
-        assert len(free) + len(used) == self.num_blocks, "block neither free nor in use"
+        lru = set(self.lru)
+        assert len(lru) == len(self.lru), "block twice on the eviction list"
+        assert not (free & used) and not (lru & used) and not (free & lru), "block in two of free/evictable/used"
+        assert len(free) + len(lru) + len(used) == self.num_blocks, "block neither free, evictable nor in use"
+        # digest registry: a bijection between digests and registered blocks
+        assert len(self.cached) == sum(d is not None for d in self.block_digest)
+        for d, b in self.cached.items():
+            assert self.block_digest[b] == d, "registry and block digests disagree"
+        for b in free:
+            assert self.block_digest[b] is None, "registered block on the free stack"
+        for b in lru:
+            assert self.block_digest[b] is not None, "unregistered block on the eviction list"
+        # every sequence's chain recomputed from its token ids, and every
+        # registered block it holds carries the digest of its position
+        bs = self.block_size
+        for sid, t in self.tables.items():
+            known, digests = self.tokens[sid], self.digests[sid]
+            assert len(known) <= self.lens[sid] and len(digests) <= self.lens[sid] // bs
+            d = ZERO_DIGEST
+            for i, di in enumerate(digests):
+                d = block_digest(d, self.salt[sid], known[i * bs:(i + 1) * bs])
+                assert d == di, "sequence chain digest does not recompute"
+                if self.block_digest[t[i]] is not None:
+                    assert self.block_digest[t[i]] == di, "shared block registered under another chain"
