@@ -199,27 +199,84 @@ int32_t pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* ini
                       pkv_block_manager** out);
 void pkv_bm_destroy(pkv_block_manager* bm);
 
-/* Register an empty sequence (L = 0).  Error if the id exists. */
+/* Register an empty sequence (L = 0, salt 0).  Error if the id exists. */
 int32_t pkv_bm_add_seq(pkv_block_manager* bm, int64_t seq_id);
 
+/* ---- Prefix cache ---------------------------------------------------- */
+/* Chained block digests with a tenant salt ([aitalk] the closing part on  */
+/* vLLM's automatic prefix caching, and the paragraph on cache salting):   */
+/* every full block whose token ids are known gets                         */
+/*   digest = SHA-256(parent digest (32 bytes; zeros for the first block)  */
+/*                    || salt (uint64, little-endian)                      */
+/*                    || its block_size token ids (int32, little-endian))  */
+/* so equal token prefixes under equal salts give equal chains.            */
+/* Policy (the pages leave it open):                                       */
+/*   - a block is registered under its digest when it fills, if its ids    */
+/*     (given to pkv_bm_append_slots / pkv_bm_stage_step with every        */
+/*     append since the sequence began) and its parent's digest are known, */
+/*     and no other block holds that digest (else it is a duplicate and    */
+/*     stays unregistered);                                                */
+/*   - a registered block whose refcount drops to 0 keeps its digest and  */
+/*     joins an eviction list, oldest first; a released sequence adds its  */
+/*     registered blocks from its last block to its first;                 */
+/*   - new blocks come from the free stack; only when it is empty is the  */
+/*     oldest evictable block taken (its digest is forgotten).             */
+/*   - a registered block is immutable: a write into it (after a fork     */
+/*     inside it) always copies it first, reported as a copy pair; if the */
+/*     writer was its last holder it becomes evictable after the call.    */
+/*     pkv_bm_num_free counts both;                                        */
+/*   - without token ids nothing registers and the policy above is the    */
+/*     plain free-stack one.                                               */
+
+/* Digest of one block (host): parent = 32 bytes or NULL for zeros;       */
+/* tokens [n_tokens]; out = 32 bytes.  Lets a router compute the keys a    */
+/* prompt would look up.                                                   */
+int32_t pkv_block_digest(const uint8_t* parent, uint64_t salt, const int32_t* tokens, int32_t n_tokens,
+                         uint8_t* out);
+
+/* Register sequence `seq_id` for a prompt tokens[0..n_tokens): its        */
+/* leading full blocks are looked up in order and each registered one is  */
+/* shared (refcount + 1; taken off the eviction list at 0) until the first */
+/* miss.  The sequence starts at L = *n_cached_out (a multiple of          */
+/* block_size, <= n_tokens) with salt `salt`; the caller appends the rest  */
+/* of the prompt with its ids.  Never allocates; error if the id exists.   */
+int32_t pkv_bm_add_seq_cached(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                              uint64_t salt, int32_t* n_cached_out);
+
+/* Prompt tokens pkv_bm_add_seq_cached would share now (>= 0), changing    */
+/* nothing; negative status on error.                                      */
+int32_t pkv_bm_match_prefix(const pkv_block_manager* bm, const int32_t* tokens, int32_t n_tokens, uint64_t salt);
+
+/* Registered blocks (in use or evictable).                                */
+int32_t pkv_bm_num_cached(const pkv_block_manager* bm);
+/* Evictable blocks, oldest (next evicted) first; returns the count;       */
+/* PKV_ERR_CAPACITY if capacity is too small.                              */
+int32_t pkv_bm_evictable(const pkv_block_manager* bm, int32_t* out, int32_t capacity);
+/* 1 and the 32-byte digest in out if `block` is registered, else 0.       */
+int32_t pkv_bm_cached_digest(const pkv_block_manager* bm, int32_t block, uint8_t* out);
+
 /* Register `child` sharing the first ceil(num_tokens / bs) blocks of      */
-/* `parent` (refcount + 1 each), with L = num_tokens <= L(parent).         */
+/* `parent` (refcount + 1 each), with L = num_tokens <= L(parent); it      */
+/* inherits the parent's salt, known token ids and digests up to there.    */
 int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child, int32_t num_tokens);
 
 /* Reserve slots for new tokens.                                           */
 /* seq_ids     : [n_seqs] distinct registered ids                          */
 /* num_tokens  : [n_seqs] tokens per sequence (>= 0), or NULL for 1 each   */
+/* token_ids   : the new tokens' ids, in slot order (sequence-major), or    */
+/*               NULL (then the sequences' digest chains end here)          */
 /* slot_mapping_out : [slot_capacity]; receives the slots, sequence-major  */
 /* cow_pairs_out    : [cow_capacity][2]; receives (src, dst) block copies  */
 /*                    that must run before the tokens are written          */
 /* *n_slots_out, *n_cow_out : counts written (either may be NULL)          */
 int32_t pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs,
-                            const int32_t* num_tokens, int32_t* slot_mapping_out, int32_t slot_capacity,
+                            const int32_t* num_tokens, const int32_t* token_ids, int32_t* slot_mapping_out,
+                            int32_t slot_capacity,
                             int32_t* n_slots_out, int32_t* cow_pairs_out, int32_t cow_capacity,
                             int32_t* n_cow_out);
 
-/* Release a sequence: refcount - 1 on each block, blocks reaching 0 go   */
-/* back to the free pool.                                                  */
+/* Release a sequence: refcount - 1 on each block; blocks reaching 0 go  */
+/* back to the free pool (registered ones to the eviction list).           */
 int32_t pkv_bm_free_seq(pkv_block_manager* bm, int64_t seq_id);
 
 /* Export block tables and lengths.                                        */
@@ -242,6 +299,8 @@ int32_t pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids,
 /*   first call on a table, a different table or width, or full != 0     */
 /*   writes every used entry.  Entries past ceil(L / bs) are not written. */
 /* The table must only be written by this function between calls.        */
+/* token_ids     : host [n_seqs], the new tokens' ids, or NULL (as in     */
+/*                 pkv_bm_append_slots)                                   */
 /* stage         : pinned host memory (hipHostMalloc / pinned tensor) of  */
 /*                 stage_capacity int32, at least                         */
 /*                 pkv_bm_stage_capacity(n_seqs, max_blocks_per_seq); the */
@@ -252,7 +311,8 @@ int32_t pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids,
 /* *n_cow_out    : pairs written; *max_len_out: largest context length    */
 /* All device buffers are int32.  Errors before the reservation leave the */
 /* manager unchanged.                                                     */
-int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs, int32_t* stage,
+int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs, const int32_t* token_ids,
+                          int32_t* stage,
                           int32_t stage_capacity, int32_t* block_tables, int32_t max_blocks_per_seq,
                           int32_t* context_lens, int32_t* slot_mapping, int32_t* cow_pairs, int32_t cow_capacity,
                           int32_t full, int32_t* n_cow_out, int32_t* max_len_out, void* stream);

@@ -58,6 +58,11 @@ of different tenants apart.  Readings where they are silent:
 * a new block comes from the free stack; only when that is empty is the
   oldest evictable block taken, and its digest forgotten; a lookup hit on
   an evictable block takes it off the list;
+* a registered block is immutable (its digest stands for its tokens): a
+  write into one, possible after a fork inside it, copies it first even if
+  the writer is its only holder; a block released that way joins the
+  eviction list after the whole call, so no copy in the call can read a
+  block the same call hands out again;
 * token ids are recorded only while they are given with every append; an
   append without ids ends the sequence's chain (its later blocks are never
   registered).
@@ -228,6 +233,9 @@ class BlockManagerModel:
             del m[sid]
 
     # --------------------------------------------------------------- append
+    def _must_copy(self, b, dropped):
+        return self.block_digest[b] is not None or self.refcount[b] - dropped.get(b, 0) > 1
+
     def blocks_needed(self, sids, ntoks):
         bs = self.block_size
         need = 0
@@ -238,7 +246,7 @@ class BlockManagerModel:
             L = self.lens[sid]
             if L % bs:
                 last = self.tables[sid][L // bs]
-                if self.refcount[last] - dropped.get(last, 0) > 1:
+                if self._must_copy(last, dropped):
                     need += 1
                     dropped[last] = dropped.get(last, 0) + 1
             need += _cdiv(L + n, bs) - _cdiv(L, bs)
@@ -253,7 +261,7 @@ class BlockManagerModel:
             if n == 0 or L % bs == 0:
                 continue
             last = self.tables[sid][L // bs]
-            if self.refcount[last] - dropped.get(last, 0) > 1:
+            if self._must_copy(last, dropped):
                 n_cow += 1
                 dropped[last] = dropped.get(last, 0) + 1
         return n_cow
@@ -289,7 +297,7 @@ class BlockManagerModel:
         if self.blocks_needed(sids, ntoks) > self._available():
             raise OutOfBlocks("not enough free blocks")
         bs = self.block_size
-        slots, pairs = [], []
+        slots, pairs, released = [], [], []
         for sid, n in zip(sids, ntoks):
             table = self.tables[sid]
             known = self.tokens[sid]
@@ -301,18 +309,21 @@ class BlockManagerModel:
                     table.append(b)
                 else:
                     old = table[L // bs]
-                    if self.refcount[old] > 1:
+                    if self._must_copy(old, {}):
                         b = self._take()
                         pairs.append((old, b))
                         self.refcount[old] -= 1
                         self.refcount[b] = 1
                         table[L // bs] = b
+                        if self.refcount[old] == 0:  # registered, last holder gone
+                            released.append(old)
                 if token_ids is not None and len(known) == L:
                     known.append(token_ids[len(slots)])
                 slots.append(table[L // bs] * bs + L % bs)
                 self.lens[sid] = L + 1
                 if (L + 1) % bs == 0:
                     self._complete(sid, L // bs)
+        self.lru.extend(released)
         return slots, pairs
 
     def _complete(self, sid, i):

@@ -44,6 +44,7 @@ class OracleRun:
             )
         self.sources = {}  # sid -> list of (key, row)
         self.cow_log = []
+        self.admitted = {}  # sid -> prompt tokens found in the prefix cache
         self._kv_cache = {}
         self.step_done = -1
         for op in workload.setup_ops:
@@ -70,20 +71,29 @@ class OracleRun:
         elif kind == "append":
             _, sids, ntoks, key = op
             self._append(sids, ntoks, key)
+        elif kind == "admit":
+            _, sid, tokens, key, salt = op
+            tokens = [int(t) for t in tokens]
+            n = self.bm.add_seq_cached(sid, tokens, salt)
+            self.admitted[sid] = n
+            # the cached positions hold the same values as the prompt's rows
+            self.sources[sid] = [(key, i) for i in range(n)]
+            self._append([sid], [len(tokens) - n], key, token_ids=tokens[n:], first_row=n)
         else:
             raise ValueError(op)
 
-    def _append(self, sids, ntoks, key):
-        slots, pairs = self.bm.append_slots(sids, ntoks)
+    def _append(self, sids, ntoks, key, token_ids=None, first_row=0):
+        slots, pairs = self.bm.append_slots(sids, ntoks, token_ids=token_ids)
         self.cow_log.append(pairs)
-        row = 0
+        row = first_row
         for sid, n in zip(sids, ntoks):
             self.sources[sid].extend((key, row + i) for i in range(n))
             row += n
         if self.materialize:
             _pool.copy_blocks(self.k_pool, self.v_pool, pairs)
             k, v = self._kv(key)
-            _pool.append(self.k_pool, self.v_pool, _storage(k), _storage(v), slots)
+            end = first_row + len(slots)
+            _pool.append(self.k_pool, self.v_pool, _storage(k[first_row:end]), _storage(v[first_row:end]), slots)
             self._kv_cache.pop(key, None)
         return slots, pairs
 
@@ -91,7 +101,8 @@ class OracleRun:
         """Decode step ``k``: append one token per decode sequence; returns (slots, pairs)."""
         sids = self.w.decode_seqs
         key = ("step", k)
-        out = self._append(sids, [1] * len(sids), key)
+        ids = self.w.step_tokens(k) if hasattr(self.w, "step_tokens") else None
+        out = self._append(sids, [1] * len(sids), key, token_ids=None if ids is None else [int(t) for t in ids])
         self.step_done = k
         return out
 

@@ -55,6 +55,8 @@ lib = C.CDLL(LIB_PATH)
 _i32, _i64, _sz, _f32, _vp = C.c_int32, C.c_int64, C.c_size_t, C.c_float, C.c_void_p
 _pi32 = C.POINTER(C.c_int32)
 _pi64 = C.POINTER(C.c_int64)
+_u64 = C.c_uint64
+_pu8 = C.POINTER(C.c_uint8)
 
 _SIGS = {
     "pkv_last_error": (C.c_char_p, []),
@@ -72,7 +74,7 @@ _SIGS = {
     "pkv_bm_destroy": (None, [_vp]),
     "pkv_bm_add_seq": (_i32, [_vp, _i64]),
     "pkv_bm_fork": (_i32, [_vp, _i64, _i64, _i32]),
-    "pkv_bm_append_slots": (_i32, [_vp, _pi64, _i32, _pi32, _pi32, _i32, _pi32, _pi32, _i32, _pi32]),
+    "pkv_bm_append_slots": (_i32, [_vp, _pi64, _i32, _pi32, _pi32, _pi32, _i32, _pi32, _pi32, _i32, _pi32]),
     "pkv_bm_free_seq": (_i32, [_vp, _i64]),
     "pkv_bm_block_tables": (_i32, [_vp, _pi64, _i32, _i32, _pi32, _pi32]),
     "pkv_bm_num_free": (_i32, [_vp]),
@@ -81,8 +83,14 @@ _SIGS = {
     "pkv_bm_num_seqs": (_i32, [_vp]),
     "pkv_bm_free_stack": (_i32, [_vp, _pi32, _i32]),
     "pkv_bm_stage_step": (
-        _i32, [_vp, _pi64, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _pi32, _pi32, _vp]),
+        _i32, [_vp, _pi64, _i32, _pi32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _pi32, _pi32, _vp]),
     "pkv_bm_stage_capacity": (_i32, [_i32, _i32]),
+    "pkv_block_digest": (_i32, [_pu8, _u64, _pi32, _i32, _pu8]),
+    "pkv_bm_add_seq_cached": (_i32, [_vp, _i64, _pi32, _i32, _u64, _pi32]),
+    "pkv_bm_match_prefix": (_i32, [_vp, _pi32, _i32, _u64]),
+    "pkv_bm_num_cached": (_i32, [_vp]),
+    "pkv_bm_evictable": (_i32, [_vp, _pi32, _i32]),
+    "pkv_bm_cached_digest": (_i32, [_vp, _i32, _pu8]),
 }
 
 for _name, (_res, _args) in _SIGS.items():

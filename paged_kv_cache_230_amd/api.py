@@ -174,8 +174,44 @@ def _i32p(a: np.ndarray | None):
     return a.ctypes.data_as(C.POINTER(C.c_int32)) if a is not None else None
 
 
+def _ids32(token_ids, count: int):
+    if token_ids is None:
+        return None
+    a = np.ascontiguousarray(token_ids, dtype=np.int64)
+    if a.shape != (count,):
+        raise ValueError(f"token_ids must hold {count} ids")
+    if a.size and (a.min() < -(2 ** 31) or a.max() >= 2 ** 31):
+        raise ValueError("token ids must fit in int32")
+    return a.astype(np.int32)
+
+
+def _u8p(a: np.ndarray | None):
+    return a.ctypes.data_as(C.POINTER(C.c_uint8)) if a is not None else None
+
+
+def block_digest(parent: bytes | None, salt: int, tokens) -> bytes:
+    """Prefix-cache digest of one block (pkv_block_digest)."""
+    toks = _ids32(list(tokens), len(tokens))
+    par = None
+    if parent is not None:
+        if len(parent) != 32:
+            raise ValueError("parent digest must be 32 bytes")
+        par = np.frombuffer(bytes(parent), np.uint8).copy()
+    out = np.zeros(32, np.uint8)
+    N.check(N.lib.pkv_block_digest(_u8p(par), _salt(salt), _i32p(toks), toks.shape[0], _u8p(out)))
+    return out.tobytes()
+
+
+def _salt(salt: int) -> int:
+    salt = int(salt)
+    if not 0 <= salt < 2 ** 64:
+        raise ValueError("salt must fit in 64 unsigned bits")
+    return salt
+
+
 class BlockManager:
-    """Host block manager (pkv_bm_*): free pool, refcounts, fork, copy-on-write."""
+    """Host block manager (pkv_bm_*): free pool, refcounts, fork, copy-on-write,
+    and prefix caching by chained block digests."""
 
     def __init__(self, num_blocks: int, block_size: int, initial_free_order=None):
         self.num_blocks = int(num_blocks)
@@ -203,18 +239,46 @@ class BlockManager:
     def add_seq(self, seq_id: int):
         N.check(N.lib.pkv_bm_add_seq(self._h, int(seq_id)))
 
+    def add_seq_cached(self, seq_id: int, tokens, salt: int = 0) -> int:
+        """Register a sequence for a prompt, sharing its cached leading blocks;
+        returns the number of prompt tokens already cached."""
+        toks = _ids32(list(tokens), len(tokens))
+        n = C.c_int32(0)
+        N.check(N.lib.pkv_bm_add_seq_cached(self._h, int(seq_id), _i32p(toks), toks.shape[0], _salt(salt),
+                                            C.byref(n)))
+        return n.value
+
+    def match_prefix(self, tokens, salt: int = 0) -> int:
+        toks = _ids32(list(tokens), len(tokens))
+        return N.check(N.lib.pkv_bm_match_prefix(self._h, _i32p(toks), toks.shape[0], _salt(salt)))
+
+    def num_cached(self) -> int:
+        return N.check(N.lib.pkv_bm_num_cached(self._h))
+
+    def evictable(self) -> list[int]:
+        buf = np.empty(max(self.num_blocks, 1), np.int32)
+        n = N.check(N.lib.pkv_bm_evictable(self._h, _i32p(buf), buf.shape[0]))
+        return buf[:n].tolist()
+
+    def cached_digest(self, block: int) -> bytes | None:
+        out = np.zeros(32, np.uint8)
+        return out.tobytes() if N.check(N.lib.pkv_bm_cached_digest(self._h, int(block), _u8p(out))) else None
+
     def fork(self, parent: int, child: int, num_tokens: int):
         N.check(N.lib.pkv_bm_fork(self._h, int(parent), int(child), int(num_tokens)))
 
     def free_seq(self, seq_id: int):
         N.check(N.lib.pkv_bm_free_seq(self._h, int(seq_id)))
 
-    def append_slots(self, seq_ids, num_tokens=None):
-        """Returns ``(slots int32[T], cow_pairs int32[n][2])`` (NumPy views valid until the next call)."""
+    def append_slots(self, seq_ids, num_tokens=None, token_ids=None):
+        """Returns ``(slots int32[T], cow_pairs int32[n][2])`` (NumPy views valid until the next call).
+
+        ``token_ids`` (T ids in slot order, or None) feed the prefix cache."""
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         n = ids.shape[0]
         nt = None if num_tokens is None else np.ascontiguousarray(num_tokens, dtype=np.int32)
         total = n if nt is None else int(nt.sum())
+        tid = _ids32(token_ids, total)
         if self._slots.shape[0] < max(total, 1):
             self._slots = np.empty(max(total, 1), np.int32)
         cow_cap = n
@@ -223,7 +287,7 @@ class BlockManager:
         ns, nc = C.c_int32(0), C.c_int32(0)
         N.check(
             N.lib.pkv_bm_append_slots(
-                self._h, _i64p(ids), n, _i32p(nt), _i32p(self._slots), self._slots.shape[0], C.byref(ns),
+                self._h, _i64p(ids), n, _i32p(nt), _i32p(tid), _i32p(self._slots), self._slots.shape[0], C.byref(ns),
                 _i32p(self._pairs), self._pairs.shape[0] // 2, C.byref(nc),
             )
         )
@@ -243,17 +307,20 @@ class BlockManager:
                                           _i32p(lens_out)))
         return tables_out, lens_out
 
-    def stage_step(self, seq_ids, stage, block_tables, context_lens, slot_mapping, cow_pairs, full=False):
+    def stage_step(self, seq_ids, stage, block_tables, context_lens, slot_mapping, cow_pairs, full=False,
+                   token_ids=None):
         """One decode step's bookkeeping, staged to the device without copies.
 
         ``stage``: pinned int32 CPU tensor of at least ``stage_capacity``
         entries (alternate two and wait for the GPU before reusing one);
         ``block_tables`` [n][max_blocks], ``context_lens`` [n],
         ``slot_mapping`` [n], ``cow_pairs`` [n][2]: int32 device tensors.
+        ``token_ids``: the new tokens' ids ([n], host) for the prefix cache.
         Returns ``(n_cow, max_len)``; the work runs on the current stream.
         """
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         n = ids.shape[0]
+        tid = _ids32(token_ids, n)
         if not (stage.dtype == torch.int32 and stage.is_pinned() and stage.is_contiguous()):
             raise ValueError("stage must be a contiguous pinned int32 CPU tensor")
         dev = block_tables.device
@@ -269,7 +336,7 @@ class BlockManager:
         n_cow, max_len = C.c_int32(0), C.c_int32(0)
         N.check(
             N.lib.pkv_bm_stage_step(
-                self._h, _i64p(ids), n, C.c_void_p(stage.data_ptr()), stage.numel(), _ptr(block_tables),
+                self._h, _i64p(ids), n, _i32p(tid), C.c_void_p(stage.data_ptr()), stage.numel(), _ptr(block_tables),
                 block_tables.shape[1], _ptr(context_lens), _ptr(slot_mapping), _ptr(cow_pairs), cow_pairs.shape[0],
                 int(bool(full)), C.byref(n_cow), C.byref(max_len), _stream(dev),
             )

@@ -26,6 +26,7 @@ class PagedKVCache:
         self.k_cache, self.v_cache = new_pools(num_blocks, num_kv_heads, head_dim, block_size, dtype, self.device)
         self.bm = BlockManager(num_blocks, block_size, free_order)
         self.cow_log = []
+        self.admitted = {}  # sid -> prompt tokens found in the prefix cache
 
     # ------------------------------------------------------------- sequences
     def add_seq(self, sid):
@@ -37,9 +38,20 @@ class PagedKVCache:
     def free_seq(self, sid):
         self.bm.free_seq(sid)
 
-    def append(self, sids, ntoks, k, v):
+    def admit(self, sid, tokens, k, v, salt=0):
+        """Cached admission of a prompt: share its cached leading blocks, then
+        append the rest (K/V rows ``k[i]``, ``v[i]`` for prompt position i).
+        Returns the number of prompt tokens found in the cache."""
+        n = self.bm.add_seq_cached(sid, tokens, salt)
+        self.admitted[sid] = n
+        rest = len(tokens) - n
+        if rest:
+            self.append([sid], [rest], k[n:], v[n:], token_ids=np.asarray(tokens)[n:])
+        return n
+
+    def append(self, sids, ntoks, k, v, token_ids=None):
         """Reserve slots, run copy-on-write copies, then write the tokens' K/V."""
-        slots, pairs = self.bm.append_slots(sids, ntoks)
+        slots, pairs = self.bm.append_slots(sids, ntoks, token_ids=token_ids)
         self.cow_log.append(pairs.copy())
         if pairs.shape[0]:
             paged_kv_copy_blocks(self.k_cache, self.v_cache, torch.from_numpy(pairs.copy()).to(self.device))
@@ -66,6 +78,10 @@ class PagedKVCache:
             _, sids, ntoks, key = op
             k, v = kv_fn(key)
             self.append(sids, ntoks, k, v)
+        elif kind == "admit":
+            _, sid, tokens, key, salt = op
+            k, v = kv_fn(key)
+            self.admit(sid, tokens, k, v, salt)
         else:
             raise ValueError(f"unknown operation {op!r}")
 

@@ -19,6 +19,27 @@
 //     call order;
 //   * every call validates and counts what it needs before mutating, so an
 //     error leaves the state unchanged.
+//
+// Prefix caching by chained block digests ("PagedAttention et RadixAttention
+// : parlons de KV Cache", on vLLM's automatic prefix caching and on cache
+// salting): a full block whose token ids are known gets
+// SHA-256(parent digest || salt || token ids) and is registered under it; a
+// cached admission walks a prompt's full blocks and shares each registered
+// one until the first miss; the salt keeps tenants apart.  Policy:
+//   * a block registers when it fills, if its ids and its parent's digest are
+//     known and the digest is not registered yet (else it is a duplicate and
+//     stays unregistered);
+//   * a registered block released to refcount 0 keeps its digest and joins an
+//     eviction list (oldest first); a released sequence adds its registered
+//     blocks from the last to the first, so chains lose their deepest blocks
+//     first;
+//   * allocation pops the free stack, and takes (and unregisters) the oldest
+//     evictable block only when the stack is empty; a cache hit takes an
+//     evictable block off the list;
+//   * a registered block is immutable: a write into one (possible after a
+//     fork inside it) copies it first even for its only holder; a block
+//     released that way joins the eviction list after the whole call, so no
+//     copy of the call reads a block the same call hands out again.
 #include <algorithm>
 #include <cstdint>
 #include <new>
@@ -27,11 +48,18 @@
 #include <vector>
 
 #include "pkv_status.h"
+#include "sha256.h"
 
 struct pkv_block_manager {
   struct Seq {
     std::vector<int32_t> table;
     int32_t len = 0;
+    // Prefix cache: salt, the known leading token ids (they stop being
+    // recorded once an append comes without ids) and the chain digests of
+    // the leading full blocks.
+    uint64_t salt = 0;
+    std::vector<int32_t> tokens;
+    std::vector<pkv::Digest> digests;
     // Device mirror (pkv_bm_stage_step): row of the device table this
     // sequence was last written to (-1: none), entries written there, and the
     // lowest entry changed since (a copy-on-write replacement).
@@ -44,13 +72,21 @@ struct pkv_block_manager {
   std::vector<int32_t> free_stack;  // back() is handed out next
   std::vector<int32_t> refcount;
   std::unordered_map<int64_t, Seq> seqs;
+  // Prefix cache: digest registry, each block's digest, and the eviction
+  // list of registered blocks at refcount 0 (a doubly linked list over block
+  // ids, head = oldest).
+  std::unordered_map<pkv::Digest, int32_t, pkv::DigestHash> cached;
+  std::vector<pkv::Digest> block_digest;
+  std::vector<uint8_t> registered;
+  std::vector<int32_t> lru_prev, lru_next;
+  int32_t lru_head = -1, lru_tail = -1, lru_size = 0;
   // Device table the mirror state refers to, and the sequence whose entries
   // each of its rows last received.
   const void* mirror_table = nullptr;
   int32_t mirror_width = 0;
   std::vector<int64_t> row_owner;
-  // Scratch reused by pkv_bm_stage_step.
-  std::vector<int32_t> scratch_slots, scratch_pairs;
+  // Scratch reused by pkv_bm_stage_step and pkv_bm_append_slots.
+  std::vector<int32_t> scratch_slots, scratch_pairs, scratch_released;
 };
 
 namespace {
@@ -60,6 +96,74 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int32_t check_handle(const pkv_block_manager* bm) {
   if (!bm) return pkv::fail(PKV_ERR_INVALID_ARG, "null block manager handle");
   return PKV_OK;
+}
+
+using BM = pkv_block_manager;
+
+void lru_push_back(BM* bm, int32_t b) {
+  bm->lru_prev[b] = bm->lru_tail;
+  bm->lru_next[b] = -1;
+  if (bm->lru_tail >= 0) bm->lru_next[bm->lru_tail] = b;
+  else bm->lru_head = b;
+  bm->lru_tail = b;
+  ++bm->lru_size;
+}
+
+void lru_remove(BM* bm, int32_t b) {
+  const int32_t p = bm->lru_prev[b], n = bm->lru_next[b];
+  if (p >= 0) bm->lru_next[p] = n;
+  else bm->lru_head = n;
+  if (n >= 0) bm->lru_prev[n] = p;
+  else bm->lru_tail = p;
+  bm->lru_prev[b] = bm->lru_next[b] = -1;
+  --bm->lru_size;
+}
+
+int64_t available(const BM* bm) { return static_cast<int64_t>(bm->free_stack.size()) + bm->lru_size; }
+
+// A fresh block: the free stack first, else the oldest evictable block,
+// whose digest is forgotten.  The caller has checked availability.
+int32_t take_block(BM* bm) {
+  if (!bm->free_stack.empty()) {
+    const int32_t b = bm->free_stack.back();
+    bm->free_stack.pop_back();
+    return b;
+  }
+  const int32_t b = bm->lru_head;
+  lru_remove(bm, b);
+  bm->cached.erase(bm->block_digest[b]);
+  bm->registered[b] = 0;
+  return b;
+}
+
+// Block i of s has just filled: give it its chain digest and register it.
+void complete_block(BM* bm, BM::Seq& s, int32_t i) {
+  const int32_t bs = bm->block_size;
+  if (static_cast<int64_t>(s.tokens.size()) < static_cast<int64_t>(i + 1) * bs ||
+      static_cast<int32_t>(s.digests.size()) != i)
+    return;
+  const pkv::Digest parent = i ? s.digests[i - 1] : pkv::Digest{};
+  const pkv::Digest d = pkv::block_digest(parent, s.salt, s.tokens.data() + static_cast<size_t>(i) * bs, bs);
+  s.digests.push_back(d);
+  const int32_t b = s.table[i];
+  if (bm->cached.emplace(d, b).second) {
+    bm->block_digest[b] = d;
+    bm->registered[b] = 1;
+  }
+}
+
+// Registered blocks for the leading full blocks of a prompt, up to the first miss.
+void match_prefix(const BM* bm, const int32_t* tokens, int32_t n, uint64_t salt, std::vector<int32_t>* blocks,
+                  std::vector<pkv::Digest>* digests) {
+  const int32_t bs = bm->block_size;
+  pkv::Digest d{};
+  for (int32_t i = 0; i < n / bs; ++i) {
+    d = pkv::block_digest(d, salt, tokens + static_cast<size_t>(i) * bs, bs);
+    auto it = bm->cached.find(d);
+    if (it == bm->cached.end()) break;
+    blocks->push_back(it->second);
+    if (digests) digests->push_back(d);
+  }
 }
 
 }  // namespace
@@ -80,6 +184,10 @@ int32_t pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* ini
   bm->num_blocks = num_blocks;
   bm->block_size = block_size;
   bm->refcount.assign(num_blocks, 0);
+  bm->block_digest.resize(num_blocks);
+  bm->registered.assign(num_blocks, 0);
+  bm->lru_prev.assign(num_blocks, -1);
+  bm->lru_next.assign(num_blocks, -1);
   bm->free_stack.resize(num_blocks);
   if (initial_free_order) {
     std::vector<char> seen(num_blocks, 0);
@@ -101,10 +209,50 @@ int32_t pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* ini
 
 void pkv_bm_destroy(pkv_block_manager* bm) { delete bm; }
 
-int32_t pkv_bm_add_seq(pkv_block_manager* bm, int64_t seq_id) {
+int32_t pkv_bm_add_seq_cached(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                              uint64_t salt, int32_t* n_cached_out) {
   if (int32_t e = check_handle(bm)) return e;
   if (bm->seqs.count(seq_id)) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %lld already exists", (long long)seq_id);
-  bm->seqs.emplace(seq_id, pkv_block_manager::Seq{});
+  if (n_tokens < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "n_tokens < 0");
+  if (n_tokens > 0 && !tokens) return pkv::fail(PKV_ERR_INVALID_ARG, "tokens is null");
+  pkv_block_manager::Seq s;
+  match_prefix(bm, tokens, n_tokens, salt, &s.table, &s.digests);
+  for (int32_t b : s.table) {
+    if (bm->refcount[b] == 0) lru_remove(bm, b);
+    bm->refcount[b] += 1;
+  }
+  s.len = static_cast<int32_t>(s.table.size()) * bm->block_size;
+  s.salt = salt;
+  if (s.len > 0) s.tokens.assign(tokens, tokens + s.len);
+  const int32_t n = s.len;
+  bm->seqs.emplace(seq_id, std::move(s));
+  if (n_cached_out) *n_cached_out = n;
+  return pkv::ok();
+}
+
+int32_t pkv_bm_add_seq(pkv_block_manager* bm, int64_t seq_id) {
+  return pkv_bm_add_seq_cached(bm, seq_id, nullptr, 0, 0, nullptr);
+}
+
+int32_t pkv_bm_match_prefix(const pkv_block_manager* bm, const int32_t* tokens, int32_t n_tokens, uint64_t salt) {
+  if (int32_t e = check_handle(bm)) return e;
+  if (n_tokens < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "n_tokens < 0");
+  if (n_tokens > 0 && !tokens) return pkv::fail(PKV_ERR_INVALID_ARG, "tokens is null");
+  std::vector<int32_t> blocks;
+  match_prefix(bm, tokens, n_tokens, salt, &blocks, nullptr);
+  pkv::ok();
+  return static_cast<int32_t>(blocks.size()) * bm->block_size;
+}
+
+int32_t pkv_block_digest(const uint8_t* parent, uint64_t salt, const int32_t* tokens, int32_t n_tokens,
+                         uint8_t* out) {
+  if (!out) return pkv::fail(PKV_ERR_INVALID_ARG, "out is null");
+  if (n_tokens < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "n_tokens < 0");
+  if (n_tokens > 0 && !tokens) return pkv::fail(PKV_ERR_INVALID_ARG, "tokens is null");
+  pkv::Digest p{};
+  if (parent) std::copy(parent, parent + 32, p.begin());
+  const pkv::Digest d = pkv::block_digest(p, salt, tokens, n_tokens);
+  std::copy(d.begin(), d.end(), out);
   return pkv::ok();
 }
 
@@ -120,13 +268,19 @@ int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child, int32_
   const int64_t nshared = cdiv(num_tokens, bm->block_size);
   s.table.assign(it->second.table.begin(), it->second.table.begin() + nshared);
   s.len = num_tokens;
+  const auto& ps = it->second;
+  s.salt = ps.salt;
+  s.tokens.assign(ps.tokens.begin(), ps.tokens.begin() + std::min<size_t>(num_tokens, ps.tokens.size()));
+  s.digests.assign(ps.digests.begin(),
+                   ps.digests.begin() + std::min<size_t>(num_tokens / bm->block_size, ps.digests.size()));
   for (int32_t b : s.table) bm->refcount[b] += 1;
   bm->seqs.emplace(child, std::move(s));
   return pkv::ok();
 }
 
 int32_t pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs,
-                            const int32_t* num_tokens, int32_t* slot_mapping_out, int32_t slot_capacity,
+                            const int32_t* num_tokens, const int32_t* token_ids, int32_t* slot_mapping_out,
+                            int32_t slot_capacity,
                             int32_t* n_slots_out, int32_t* cow_pairs_out, int32_t cow_capacity,
                             int32_t* n_cow_out) {
   if (int32_t e = check_handle(bm)) return e;
@@ -164,7 +318,7 @@ int32_t pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32
     if (L % bs) {
       const int32_t last = seqp[i]->table[L / bs];
       int32_t& d = dropped[last];
-      if (bm->refcount[last] - d > 1) {
+      if (bm->registered[last] || bm->refcount[last] - d > 1) {
         ++need_cow;
         ++d;
       }
@@ -175,40 +329,43 @@ int32_t pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32
   if (need_cow > cow_capacity)
     return pkv::fail(PKV_ERR_CAPACITY, "copy-pair buffer holds %d pairs, %lld needed", cow_capacity, (long long)need_cow);
   if (need_cow > 0 && !cow_pairs_out) return pkv::fail(PKV_ERR_INVALID_ARG, "cow_pairs_out is null");
-  if (need_blocks > static_cast<int64_t>(bm->free_stack.size()))
-    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "%lld blocks needed, %zu free", (long long)need_blocks,
-                     bm->free_stack.size());
+  if (need_blocks > available(bm))
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "%lld blocks needed, %lld free", (long long)need_blocks,
+                     (long long)available(bm));
 
   // Pass 2: apply.  Cannot fail from here on.
   int32_t ns = 0, nc = 0;
+  std::vector<int32_t>& released = bm->scratch_released;
+  released.clear();
   for (int32_t i = 0; i < n_seqs; ++i) {
     pkv_block_manager::Seq& s = *seqp[i];
     const int32_t n = num_tokens ? num_tokens[i] : 1;
     for (int32_t t = 0; t < n; ++t) {
       const int32_t L = s.len;
       if (L % bs == 0) {
-        const int32_t b = bm->free_stack.back();
-        bm->free_stack.pop_back();
+        const int32_t b = take_block(bm);
         bm->refcount[b] = 1;
         s.table.push_back(b);
       } else {
         const int32_t old = s.table[L / bs];
-        if (bm->refcount[old] > 1) {
-          const int32_t b = bm->free_stack.back();
-          bm->free_stack.pop_back();
+        if (bm->refcount[old] > 1 || bm->registered[old]) {
+          const int32_t b = take_block(bm);
           cow_pairs_out[2 * nc] = old;
           cow_pairs_out[2 * nc + 1] = b;
           ++nc;
-          bm->refcount[old] -= 1;
+          if (--bm->refcount[old] == 0) released.push_back(old);  // registered; last holder gone
           bm->refcount[b] = 1;
           s.table[L / bs] = b;
           if (L / bs < s.dirty_from) s.dirty_from = L / bs;
         }
       }
+      if (token_ids && static_cast<int64_t>(s.tokens.size()) == L) s.tokens.push_back(token_ids[ns]);
       slot_mapping_out[ns++] = s.table[L / bs] * bs + L % bs;
       s.len = L + 1;
+      if ((L + 1) % bs == 0) complete_block(bm, s, L / bs);
     }
   }
+  for (int32_t b : released) lru_push_back(bm, b);
   if (n_slots_out) *n_slots_out = ns;
   if (n_cow_out) *n_cow_out = nc;
   return pkv::ok();
@@ -218,8 +375,12 @@ int32_t pkv_bm_free_seq(pkv_block_manager* bm, int64_t seq_id) {
   if (int32_t e = check_handle(bm)) return e;
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
-  for (int32_t b : it->second.table) {
-    if (--bm->refcount[b] == 0) bm->free_stack.push_back(b);
+  const auto& t = it->second.table;
+  for (int32_t b : t) {
+    if (--bm->refcount[b] == 0 && !bm->registered[b]) bm->free_stack.push_back(b);
+  }
+  for (auto r = t.rbegin(); r != t.rend(); ++r) {
+    if (bm->refcount[*r] == 0 && bm->registered[*r]) lru_push_back(bm, *r);
   }
   bm->seqs.erase(it);
   return pkv::ok();
@@ -252,7 +413,32 @@ int32_t pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids,
 
 int32_t pkv_bm_num_free(const pkv_block_manager* bm) {
   if (int32_t e = check_handle(bm)) return e;
-  return static_cast<int32_t>(bm->free_stack.size());
+  return static_cast<int32_t>(available(bm));
+}
+
+int32_t pkv_bm_num_cached(const pkv_block_manager* bm) {
+  if (int32_t e = check_handle(bm)) return e;
+  return static_cast<int32_t>(bm->cached.size());
+}
+
+int32_t pkv_bm_evictable(const pkv_block_manager* bm, int32_t* out, int32_t capacity) {
+  if (int32_t e = check_handle(bm)) return e;
+  if (capacity < bm->lru_size)
+    return pkv::fail(PKV_ERR_CAPACITY, "capacity %d < %d evictable blocks", capacity, bm->lru_size);
+  if (bm->lru_size > 0 && !out) return pkv::fail(PKV_ERR_INVALID_ARG, "out is null");
+  int32_t n = 0;
+  for (int32_t b = bm->lru_head; b >= 0; b = bm->lru_next[b]) out[n++] = b;
+  return n;
+}
+
+int32_t pkv_bm_cached_digest(const pkv_block_manager* bm, int32_t block, uint8_t* out) {
+  if (int32_t e = check_handle(bm)) return e;
+  if (block < 0 || block >= bm->num_blocks)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "block %d outside [0, %d)", block, bm->num_blocks);
+  if (!bm->registered[block]) return 0;
+  if (!out) return pkv::fail(PKV_ERR_INVALID_ARG, "out is null");
+  std::copy(bm->block_digest[block].begin(), bm->block_digest[block].end(), out);
+  return 1;
 }
 
 int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block) {
@@ -292,7 +478,8 @@ int32_t pkv_bm_stage_capacity(int32_t n_seqs, int32_t max_blocks_per_seq) {
   return static_cast<int32_t>(need);
 }
 
-int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs, int32_t* stage,
+int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs, const int32_t* token_ids,
+                          int32_t* stage,
                           int32_t stage_capacity, int32_t* block_tables, int32_t max_blocks_per_seq,
                           int32_t* context_lens, int32_t* slot_mapping, int32_t* cow_pairs, int32_t cow_capacity,
                           int32_t full, int32_t* n_cow_out, int32_t* max_len_out, void* stream) {
@@ -343,7 +530,7 @@ int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t
   bm->scratch_slots.resize(n_seqs);
   bm->scratch_pairs.resize(2 * static_cast<size_t>(n_seqs));
   int32_t ns = 0, nc = 0;
-  if (int32_t e = pkv_bm_append_slots(bm, seq_ids, n_seqs, nullptr, bm->scratch_slots.data(), n_seqs, &ns,
+  if (int32_t e = pkv_bm_append_slots(bm, seq_ids, n_seqs, nullptr, token_ids, bm->scratch_slots.data(), n_seqs, &ns,
                                       bm->scratch_pairs.data(), n_seqs, &nc))
     return e;
 

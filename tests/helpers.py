@@ -74,7 +74,7 @@ def product_cache(w, device="cuda"):
 def product_step(cache, w, k, partition_size=0):
     """Decode step k through the library: append one token per sequence, then decode."""
     kn, vn = w.kv(("step", k))
-    slots, pairs = cache.append(w.decode_seqs, [1] * w.num_seqs, kn, vn)
+    slots, pairs = cache.append(w.decode_seqs, [1] * w.num_seqs, kn, vn, token_ids=w.step_tokens(k))
     q = w.q(k).to(cache.device)
     out = cache.decode(q, w.decode_seqs, partition_size=partition_size)
     torch.cuda.synchronize()

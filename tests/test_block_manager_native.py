@@ -118,7 +118,7 @@ def test_capacity_errors_are_atomic():
     slots = np.empty(2, np.int32)
     ns = C.c_int32(-1)
     code = N.lib.pkv_bm_append_slots(n._h, ids.ctypes.data_as(C.POINTER(C.c_int64)), 1,
-                                     cnt.ctypes.data_as(C.POINTER(C.c_int32)),
+                                     cnt.ctypes.data_as(C.POINTER(C.c_int32)), None,
                                      slots.ctypes.data_as(C.POINTER(C.c_int32)), 2, C.byref(ns), None, 0, None)
     assert code == PKV_ERR_CAPACITY and n.seq_len(0) == 0 and n.num_free() == 8 and ns.value == -1
 

@@ -31,15 +31,18 @@ class Staged:
     def new_tables(self, n, dev="cuda"):
         self.tables = torch.full((n, self.maxb), -7, dtype=torch.int32, device=dev)
 
-    def step(self, bm, order, full=False):
+    def step(self, bm, order, full=False, token_ids=None):
         r = self.k % 2
         self.done[r].synchronize()
         n = len(order)
         out = bm.stage_step(order, self.stage[r], self.tables[:n] if n < self.tables.shape[0] else self.tables,
-                            self.lens[:n], self.slots[:n], self.pairs[:n], full=full)
+                            self.lens[:n], self.slots[:n], self.pairs[:n], full=full, token_ids=token_ids)
         self.done[r].record()
         self.k += 1
         return out
+
+    def step_ids(self, bm, order, token_ids):
+        return self.step(bm, order, token_ids=token_ids)
 
 
 def _check(st, order, model, slots_m, pairs_m, n_cow, what):
@@ -102,7 +105,7 @@ def test_stage_step_rejects_unpinned_stage_without_side_effects():
 
     host = np.zeros(64, np.int32)  # pageable memory
     ids = np.zeros(1, np.int64)
-    code = N.lib.pkv_bm_stage_step(bm._h, ids.ctypes.data_as(C.POINTER(C.c_int64)), 1, C.c_void_p(host.ctypes.data),
+    code = N.lib.pkv_bm_stage_step(bm._h, ids.ctypes.data_as(C.POINTER(C.c_int64)), 1, None, C.c_void_p(host.ctypes.data),
                                    64, C.c_void_p(t.data_ptr()), 4, C.c_void_p(v.data_ptr()), C.c_void_p(v.data_ptr()),
                                    C.c_void_p(p.data_ptr()), 1, 0, None, None, None)
     assert code == N.PKV_ERR_INVALID_ARG and "pinned" in N.last_error()

@@ -241,6 +241,37 @@ def test_random_run_against_token_tuple_brute_force():
     assert bm.num_cached() > 0 and len(bm.evictable()) >= 0
 
 
+def test_registered_block_is_copied_even_for_its_last_holder():
+    """A fork inside a registered block, then the parent released: the
+    child's write must not change the cached block, so it copies it; the
+    released block becomes evictable only after the call."""
+    bm = _bm(6, list(range(6)))
+    prompt = list(range(2 * BS))
+    _prefill(bm, 0, prompt)  # blocks 0, 1 registered
+    bm.fork(0, 1, 2 * BS - 1)  # child stops inside block 1
+    bm.free_seq(0)
+    assert bm.refcount[1] == 1 and bm.evictable() == []  # block 0, 1 still held by the child
+    slots, pairs = bm.append_slots([1], [1], token_ids=[99])
+    assert pairs == [(1, 2)] and slots == [2 * BS + BS - 1]
+    assert bm.evictable() == [1] and bm.refcount[1] == 0
+    assert bm.match_prefix(prompt) == 2 * BS  # the cached chain is intact
+    assert bm.match_prefix(prompt[:-1] + [99]) == 2 * BS  # the child's copy registered its own chain
+    assert bm.block_digest[2] is not None and bm.block_digest[2] != bm.block_digest[1]
+    bm.check_invariants()
+    # the block released by the copy is not handed out again in the same call
+    bm2 = _bm(4, list(range(4)))
+    _prefill(bm2, 0, prompt)  # blocks 0, 1
+    bm2.fork(0, 1, 2 * BS - 1)
+    bm2.free_seq(0)
+    bm2.add_seq(2)
+    bm2.append_slots([2], [BS])  # block 2; the stack now holds only block 3
+    with pytest.raises(OutOfBlocks):
+        bm2.append_slots([1, 2], [1, 1])  # needs a copy target and a new block: 1 is not reusable yet
+    s, p = bm2.append_slots([1], [1], token_ids=[5])
+    assert p == [(1, 3)] and bm2.evictable() == [1]
+    bm2.check_invariants()
+
+
 # ---------------------------------------------------------------- mutants
 # Each plants one plausible mistake in the oracle and checks that a pin above
 # fails under it.
@@ -263,11 +294,16 @@ def _free_head_first(self, sid):
         del m[sid]
 
 
+def _copy_only_shared(self, b, dropped):
+    return self.refcount[b] - dropped.get(b, 0) > 1
+
+
 @pytest.mark.parametrize("mutant,pin", [
     ("digest", test_chain_depends_on_every_earlier_block),
     ("salt", test_salt_separates_tenants),
     ("evict", test_eviction_is_tail_first_and_only_when_the_stack_is_empty),
-], ids=["digest-ignores-parent", "digest-ignores-salt", "evicts-head-first"])
+    ("inplace", test_registered_block_is_copied_even_for_its_last_holder),
+], ids=["digest-ignores-parent", "digest-ignores-salt", "evicts-head-first", "writes-registered-block"])
 def test_pins_catch_planted_mistakes(monkeypatch, mutant, pin):
     import oracle.block_manager as obm
 
@@ -275,7 +311,10 @@ def test_pins_catch_planted_mistakes(monkeypatch, mutant, pin):
         monkeypatch.setattr(obm, "block_digest", _digest_without_parent)
     elif mutant == "salt":
         monkeypatch.setattr(obm, "block_digest", _digest_without_salt)
-    else:
+    elif mutant == "evict":
         monkeypatch.setattr(obm.BlockManagerModel, "free_seq", _free_head_first)
+    else:
+        monkeypatch.setattr(obm.BlockManagerModel, "_must_copy", _copy_only_shared)
     with pytest.raises(AssertionError):
         pin()
+

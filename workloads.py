@@ -27,6 +27,12 @@ The five workloads follow the configurations the task is measured on:
 * ``c5_mixed_bs32_bf16`` -- 256 sequences, lengths log-uniform in
   [16, 16384], 64 q / 8 kv heads, block 32, pool sized to 95 % occupancy,
   10 consecutive append+decode steps.
+* ``c6_prefix_cache_bf16`` -- prefix caching: 50 requests whose prompts
+  are one common 2048-token system prompt plus a private user part of
+  uniform [1, 512] tokens (token ids uniform in [0, 32000)), spread over 2
+  tenants with their own salts; 2 earlier requests (one per tenant) are
+  admitted and released first, so the 50 find the system prompt's blocks
+  on the eviction list.  8B-shaped heads, block 16, 20k-block pool.
 
 Reading of the length convention: a stated context length is the number of
 tokens the decode attention reads *including* the token appended in that
@@ -39,10 +45,15 @@ Script operations (tuples):
   ``sids[i]``; K/V come from ``kv(key)`` in sequence-major order
 * ``("fork", parent, child, n)``    -- child shares parent's first n tokens
 * ``("free", sid)``                 -- release a sequence
+* ``("admit", sid, tokens, key, salt)`` -- cached admission of a prompt:
+  register ``sid`` sharing the prompt's cached leading blocks, then append
+  the rest of the prompt with its token ids; K/V of prompt position ``i``
+  are row ``i`` of ``kv(key)``
 
 After the setup script, each of ``steps`` decode steps appends one token to
 every sequence of ``decode_seqs`` (values ``kv(("step", k))``) and then
-runs decode attention with queries ``q(k)``.
+runs decode attention with queries ``q(k)``; ``step_tokens(k)`` gives the
+new tokens' ids where the workload tracks them (else None).
 """
 from __future__ import annotations
 
@@ -82,6 +93,7 @@ CONFIGS = {
     "c3_70b_32k_bf16": Config("c3_70b_32k_bf16", "bf16", 64, 8, 128, 16, 128 ** -0.5, 233),
     "c4_prefix_bf16": Config("c4_prefix_bf16", "bf16", 32, 8, 128, 16, 128 ** -0.5, 234),
     "c5_mixed_bs32_bf16": Config("c5_mixed_bs32_bf16", "bf16", 64, 8, 128, 32, 128 ** -0.5, 235, steps=10),
+    "c6_prefix_cache_bf16": Config("c6_prefix_cache_bf16", "bf16", 32, 8, 128, 16, 128 ** -0.5, 236),
 }
 
 # Stress variants of the value distribution (same shapes).  With the
@@ -91,7 +103,9 @@ CONFIGS = {
 # the hundreds (overflow / rescale path).
 VARIANTS = ("plain", "q64", "q512", "needle", "large")
 
-_KEY_TAGS = {"prefill": 1, "step": 2, "q": 3, "prefix": 4, "suffix": 5, "needle": 6}
+_KEY_TAGS = {"prefill": 1, "step": 2, "q": 3, "prefix": 4, "suffix": 5, "needle": 6, "system": 7, "user": 8,
+             "system_tokens": 9, "user_tokens": 10, "step_tokens": 11}
+VOCAB = 32000
 
 
 def _key_seed(seed: int, key: tuple) -> int:
@@ -134,6 +148,7 @@ class Workload:
             "c3_70b_32k_bf16": self._build_plain_c3,
             "c4_prefix_bf16": self._build_prefix,
             "c5_mixed_bs32_bf16": self._build_plain_c5,
+            "c6_prefix_cache_bf16": self._build_cached,
         }[self.name]
         builder(rng)
 
@@ -216,6 +231,46 @@ class Workload:
             dtype=np.int64,
         )
 
+    def _build_cached(self, rng):
+        """Cached admissions: warm-up requests admitted and released, then
+        the decode requests.  Request r belongs to tenant r % n_tenants."""
+        o = self.overrides
+        self.prefix_len = int(o.get("prefix_len", 2048))
+        n_tenants = int(o.get("n_tenants", 2))
+        warm = int(o.get("warm", n_tenants))
+        num_prompts = int(o.get("num_prompts", 50))
+        suffix_max = int(o.get("suffix_max", 512))
+        self.n_tenants = n_tenants
+        self.salts = [int(x) for x in rng.integers(1, 2 ** 62, size=n_tenants)]
+        n_req = warm + num_prompts
+        self.suffix_lens = rng.integers(1, suffix_max + 1, size=n_req).astype(np.int64)
+        self.num_blocks = int(o.get("num_blocks", 20000))
+        self.free_order = rng.permutation(self.num_blocks).astype(np.int32)
+        admit = lambda r: ("admit", r, self.prompt_tokens(r), ("prompt", r), self.salts[r % n_tenants])
+        ops = [admit(r) for r in range(warm)]
+        ops += [("free", r) for r in range(warm)]
+        ops += [admit(r) for r in range(warm, n_req)]
+        self.setup_ops = ops
+        self.decode_seqs = list(range(warm, n_req))
+        self.lengths = np.array([self.prefix_len + int(self.suffix_lens[r]) + 1 for r in self.decode_seqs],
+                                dtype=np.int64)
+        self.tracks_tokens = True
+
+    def _ints(self, key, n):
+        g = torch.Generator().manual_seed(_key_seed(self.config.seed, key))
+        return torch.randint(0, VOCAB, (n,), generator=g, dtype=torch.int64).numpy()
+
+    def prompt_tokens(self, r: int) -> np.ndarray:
+        """Token ids of request r's prompt: the system prompt, then its own part."""
+        return np.concatenate([self._ints(("system_tokens",), self.prefix_len),
+                               self._ints(("user_tokens", r), int(self.suffix_lens[r]))])
+
+    def step_tokens(self, k: int):
+        """Ids of the tokens decode step k appends (one per decode sequence), or None."""
+        if not getattr(self, "tracks_tokens", False):
+            return None
+        return self._ints(("step_tokens", k), self.num_seqs)
+
     # ----------------------------------------------------------------- values
     @property
     def num_seqs(self) -> int:
@@ -247,6 +302,15 @@ class Workload:
             T = int(self.suffix_lens[int(key[1])])
         elif key[0] == "step":
             T = self.num_seqs
+        elif key[0] == "prompt":
+            # the system prompt's rows are the same for every request
+            ks, vs = self.kv(("system",))
+            ku, vu = self.kv(("user", int(key[1])))
+            return torch.cat([ks, ku]), torch.cat([vs, vu])
+        elif key[0] == "system":
+            T = self.prefix_len
+        elif key[0] == "user":
+            T = int(self.suffix_lens[int(key[1])])
         else:
             raise KeyError(key)
         shape = (T, c.num_kv_heads, c.head_dim)
@@ -281,4 +345,6 @@ class Workload:
         for op in self.setup_ops:
             if op[0] == "append":
                 n += sum(op[2])
+            elif op[0] == "admit":
+                n += len(op[2])
         return n
