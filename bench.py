@@ -64,17 +64,72 @@ def kernel_source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic():
+def load_traffic(workload, partition):
     """HBM bytes per decode call from committed counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on this workload, in the default launch, on the current kernel
+    source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_sha():
+    if t.get("kernel_source_sha256") != kernel_source_sha() or t.get("workload") != workload or partition != 0:
         return None
     return t.get("hbm_bytes_per_decode_call")
+
+
+def prefix_cache_report(w):
+    """Host cost and effect of the prefix cache on a workload of cached
+    admissions: the admissions replayed on a fresh block manager (host only,
+    timed), hit counts, and blocks in use against private copies."""
+    import numpy as np
+
+    import paged_kv_cache_230_amd as pkv
+
+    bs = w.config.block_size
+    bm = pkv.BlockManager(w.num_blocks, bs, w.free_order)
+    n_req = prompt_tokens = cached = 0
+    t_admit = 0.0
+    for op in w.setup_ops:
+        if op[0] == "admit":
+            _, sid, tokens, _, salt = op
+            t0 = time.perf_counter()
+            n = bm.add_seq_cached(sid, tokens, salt)
+            bm.append_slots([sid], [len(tokens) - n], token_ids=tokens[n:])
+            t_admit += time.perf_counter() - t0
+            n_req += 1
+            prompt_tokens += len(tokens)
+            cached += n
+        elif op[0] == "free":
+            bm.free_seq(op[1])
+        else:
+            raise ValueError(f"prefix_cache_report expects admissions only, got {op[0]!r}")
+    in_use = w.num_blocks - bm.num_free()
+    private = sum(-(-bm.seq_len(s) // bs) for s in w.decode_seqs)
+    # digest rate alone: the full prompt chain of one request, looked up
+    toks = w.setup_ops[-1][2]
+    t0 = time.perf_counter()
+    reps = 20
+    for _ in range(reps):
+        bm.match_prefix(toks, 12345)  # a salt nobody uses: the first block misses, so hash all blocks below
+    t_miss = (time.perf_counter() - t0) / reps
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        bm.match_prefix(toks, w.setup_ops[-1][4])  # every system-prompt block hits
+    t_hit = (time.perf_counter() - t0) / reps
+    hits = bm.match_prefix(toks, w.setup_ops[-1][4]) // bs
+    return {
+        "requests": n_req,
+        "prompt_tokens": prompt_tokens,
+        "cached_tokens": cached,
+        "hit_fraction": round(cached / max(prompt_tokens, 1), 4),
+        "blocks_in_use_decode_batch": int(in_use),
+        "blocks_without_sharing": int(private),
+        "admission_host_us_per_request": round(1e6 * t_admit / max(n_req, 1), 1),
+        "lookup_us_per_block_hit": round(1e6 * t_hit / max(hits, 1), 3),
+        "lookup_us_first_block_miss": round(1e6 * t_miss, 3),
+        "note": "host-only; admission = digest lookups + reservation of the uncached rest with its ids",
+    }
 
 
 # ----------------------------------------------------------------- CPU leg
@@ -163,6 +218,7 @@ def main():
         step_v.append(vn.to(dev))
         step_q.append(w.q(k).to(dev))
 
+    step_ids = [w.step_tokens(k) for k in range(nsteps)]  # None unless the workload tracks token ids
     bm = cache.bm
     seqs = np.asarray(w.decode_seqs, np.int64)
     bs = c.block_size
@@ -198,7 +254,7 @@ def main():
         if k >= RING:
             ev1[k - RING].synchronize()  # the GPU has read record r
         t1 = time.perf_counter()
-        n_cow, max_len = bm.stage_step(seqs, stage[r], tables_d, lens_d, slots_d, pairs_d)
+        n_cow, max_len = bm.stage_step(seqs, stage[r], tables_d, lens_d, slots_d, pairs_d, token_ids=step_ids[k])
         step_lens.append(stage[r].numpy()[4 + S: 4 + 2 * S].copy())  # lengths in the record
         t2 = time.perf_counter()
         if n_cow:
@@ -236,6 +292,13 @@ def main():
     print(f"# timed {args.steps} steps in {elapsed:.4f}s; host us/step by segment: "
           + ", ".join(f"{k}={1e6 * v / args.steps:.1f}" for k, v in seg.items()), file=sys.stderr, flush=True)
 
+    # Physical K/V bytes of one call: each distinct block once (shared prefix
+    # blocks are read by many sequences but held once).
+    t_host, l_host = bm.block_tables(seqs, max_blocks)
+    used = t_host[np.arange(max_blocks)[None, :] < -(-l_host[:, None] // bs)]
+    unique_blocks = int(np.unique(used).size)
+    block_bytes = 2 * bs * c.num_kv_heads * c.head_dim * c.elem_bytes
+
     timed = range(args.warmup, nsteps)
     dec_ms = [ev0[k].elapsed_time(ev1[k]) for k in timed]
     lens_t = [step_lens[k] for k in timed]
@@ -247,7 +310,7 @@ def main():
     achieved = (sum(alg_bytes) / len(alg_bytes)) / mean_dec_s
     ms_per_step = elapsed / args.steps * 1e3
     value = sum(kv_bytes) / elapsed / 1e9
-    traffic = load_traffic()
+    traffic = load_traffic(w.name, P)
 
     result = {
         "metric": METRIC,
@@ -290,9 +353,16 @@ def main():
             "frac": round(achieved / HBM_PEAK, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_call": int(sum(alg_bytes) / len(alg_bytes)),
+            "unique_kv_block_bytes_last_call": unique_blocks * block_bytes,
         },
         "cpu_baseline": None,
     }
+    if unique_blocks < int(used.size):
+        result["roofline"]["note"] = (
+            "blocks shared by several sequences are read once per sequence but held once: logical bytes exceed "
+            "HBM traffic, so this rate is not an HBM roofline figure")
+    if any(op[0] == "admit" for op in w.setup_ops):
+        result["prefix_cache"] = prefix_cache_report(w)
     del cache, step_k, step_v, step_q, workspace
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

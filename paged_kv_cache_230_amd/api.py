@@ -177,6 +177,10 @@ def _i32p(a: np.ndarray | None):
 def _ids32(token_ids, count: int):
     if token_ids is None:
         return None
+    if isinstance(token_ids, np.ndarray) and token_ids.dtype == np.int32 and token_ids.flags.c_contiguous:
+        if token_ids.shape != (count,):
+            raise ValueError(f"token_ids must hold {count} ids")
+        return token_ids
     a = np.ascontiguousarray(token_ids, dtype=np.int64)
     if a.shape != (count,):
         raise ValueError(f"token_ids must hold {count} ids")
@@ -191,7 +195,7 @@ def _u8p(a: np.ndarray | None):
 
 def block_digest(parent: bytes | None, salt: int, tokens) -> bytes:
     """Prefix-cache digest of one block (pkv_block_digest)."""
-    toks = _ids32(list(tokens), len(tokens))
+    toks = _ids32(tokens, len(tokens))
     par = None
     if parent is not None:
         if len(parent) != 32:
@@ -242,14 +246,14 @@ class BlockManager:
     def add_seq_cached(self, seq_id: int, tokens, salt: int = 0) -> int:
         """Register a sequence for a prompt, sharing its cached leading blocks;
         returns the number of prompt tokens already cached."""
-        toks = _ids32(list(tokens), len(tokens))
+        toks = _ids32(tokens, len(tokens))
         n = C.c_int32(0)
         N.check(N.lib.pkv_bm_add_seq_cached(self._h, int(seq_id), _i32p(toks), toks.shape[0], _salt(salt),
                                             C.byref(n)))
         return n.value
 
     def match_prefix(self, tokens, salt: int = 0) -> int:
-        toks = _ids32(list(tokens), len(tokens))
+        toks = _ids32(tokens, len(tokens))
         return N.check(N.lib.pkv_bm_match_prefix(self._h, _i32p(toks), toks.shape[0], _salt(salt)))
 
     def num_cached(self) -> int:

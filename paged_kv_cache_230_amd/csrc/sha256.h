@@ -14,6 +14,10 @@
 #include <cstdint>
 #include <cstring>
 
+#if !defined(__BYTE_ORDER__) || __BYTE_ORDER__ != __ORDER_LITTLE_ENDIAN__
+#error "block digests hash int32 token ids in host byte order, which must be little-endian"
+#endif
+
 namespace pkv {
 
 using Digest = std::array<uint8_t, 32>;
@@ -126,12 +130,10 @@ class Sha256 {
     // Padding: one 1 bit, zeros up to 56 mod 64 bytes, then the bit length
     // as a 64-bit big-endian integer.
     const uint64_t bits = static_cast<uint64_t>(total_) * 8;
-    const uint8_t one = 0x80, zero = 0;
-    update(&one, 1);
-    while (fill_ != 56) update(&zero, 1);
-    uint8_t len[8];
-    for (int i = 0; i < 8; ++i) len[i] = static_cast<uint8_t>(bits >> (56 - 8 * i));
-    update(len, 8);
+    uint8_t pad[72] = {0x80};
+    const size_t zeros = (fill_ < 56 ? 56 - fill_ : 120 - fill_) - 1;
+    for (int i = 0; i < 8; ++i) pad[1 + zeros + i] = static_cast<uint8_t>(bits >> (56 - 8 * i));
+    update(pad, 1 + zeros + 8);
     Digest d;
     for (int i = 0; i < 8; ++i)
       for (int j = 0; j < 4; ++j) d[4 * i + j] = static_cast<uint8_t>(st_[i] >> (24 - 8 * j));
@@ -153,12 +155,7 @@ inline Digest block_digest(const Digest& parent, uint64_t salt, const int32_t* t
   uint8_t s[8];
   for (int i = 0; i < 8; ++i) s[i] = static_cast<uint8_t>(salt >> (8 * i));
   h.update(s, 8);
-  for (int32_t i = 0; i < n; ++i) {
-    const uint32_t t = static_cast<uint32_t>(tokens[i]);
-    const uint8_t b[4] = {static_cast<uint8_t>(t), static_cast<uint8_t>(t >> 8), static_cast<uint8_t>(t >> 16),
-                          static_cast<uint8_t>(t >> 24)};
-    h.update(b, 4);
-  }
+  h.update(tokens, static_cast<size_t>(n) * 4);  // int32 in host order = little-endian
   return h.finish();
 }
 
