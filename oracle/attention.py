@@ -23,6 +23,18 @@ formula or mention grouped-query attention; the head mapping
 ``g = h // (H_q/H_kv)`` (consecutive query heads share a kv head) and the
 scale are taken from the benchmark spec of the problem.
 
+Multi-token (chunked prefill) form: a prompt's K/V are computed during the
+prefill phase and written into the cache ("PagedAttention et RadixAttention :
+parlons de KV Cache", the part on the two independent problems: the engine
+computes the prompt's keys and values during prefill; the closing part on
+prefix caching: skipping the prefill of prefixes already seen).  Reading
+where the pages are silent: a chunk of the C newest tokens of a sequence of
+length L (their K/V already appended) is attended causally, the token at
+position p = L - C + i reading cache positions 0..p; the rows of a batch
+are packed, sequence s owning rows ``query_start[s] .. query_start[s+1]-1``.
+Each row is therefore the decode result of the same cache at context
+length p + 1.
+
 Pins (``tests/test_oracle_attention.py``): scalar brute force with
 ``math.fsum`` on tiny inputs; closed forms (L = 1 returns V_0; q = 0 or all
 keys equal returns the mean of V; constant V returns V; two tokens give a
@@ -39,7 +51,8 @@ import numpy as np
 
 from . import pool as _pool
 
-__all__ = ["dense_attention", "decode_attention", "decode_attention_bruteforce", "lse_merge", "partition_partials"]
+__all__ = ["dense_attention", "decode_attention", "decode_attention_bruteforce", "lse_merge", "partition_partials",
+           "prefill_attention"]
 
 
 def dense_attention(q_row, k_seq, v_seq, scale):
@@ -82,6 +95,40 @@ def decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale=None):
             continue
         k_seq, v_seq = _pool.gather(k_pool, v_pool, block_tables[s], L)
         out[s] = dense_attention(q64[s], _pool.to_f64(k_seq), _pool.to_f64(v_seq), scale)
+    return out
+
+
+def prefill_attention(q, k_pool, v_pool, block_tables, context_lens, query_start, scale=None):
+    """Causal attention of each sequence's newest tokens over its paged cache,
+    fp64 ``[T][H_q][d]``.
+
+    ``q``: ``[T][H_q][d]`` storage dtype, rows packed by sequence;
+    ``query_start``: ``[S+1]`` int, sequence s owning rows
+    ``query_start[s] .. query_start[s+1]-1`` = its ``C`` newest tokens, at
+    positions ``L-C .. L-1`` (``C <= L``).  Row of position p reads cache
+    positions ``0..p``.
+    """
+    q64 = _pool.to_f64(q)
+    T, Hq, d = q64.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    qs = [int(x) for x in query_start]
+    S = len(qs) - 1
+    if qs[0] != 0 or qs[-1] != T or any(qs[s + 1] < qs[s] for s in range(S)):
+        raise ValueError("query_start must rise from 0 to the number of rows")
+    out = np.zeros((T, Hq, d), dtype=np.float64)
+    for s in range(S):
+        L = int(context_lens[s])
+        C = qs[s + 1] - qs[s]
+        if C > L:
+            raise ValueError("a sequence has more new tokens than context")
+        if C == 0:
+            continue
+        k_seq, v_seq = _pool.gather(k_pool, v_pool, block_tables[s], L)
+        k64, v64 = _pool.to_f64(k_seq), _pool.to_f64(v_seq)
+        for i in range(C):
+            p = L - C + i
+            out[qs[s] + i] = dense_attention(q64[qs[s] + i], k64[: p + 1], v64[: p + 1], scale)
     return out
 
 
