@@ -142,11 +142,12 @@ int32_t paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ds
 /*                 only by fp32 rounding between splits.                  */
 /* workspace     : device scratch, at least                               */
 /*                 paged_attention_workspace_bytes(...) bytes, 256-byte   */
-/*                 aligned, required whenever num_seqs > 0: it holds the  */
-/*                 per-call work queues, the (sequence, partition) item   */
-/*                 index and the partition partials.  Any content is      */
-/*                 accepted (each call resets what it needs); calls       */
-/*                 sharing a workspace must be ordered on one stream.     */
+/*                 aligned, required whenever num_seqs > 0: it holds, per */
+/*                 (sequence, kv head), the record of the pieces a split  */
+/*                 sequence was cut into, and the pieces' partials.  Any  */
+/*                 content is accepted (each call writes what it reads);  */
+/*                 calls sharing a workspace must be ordered on one       */
+/*                 stream.                                                */
 /*                                                                        */
 /* Work distribution (balanced split): for each kv head the blocks of all */
 /* sequences form one list of T blocks; each of the N workgroups of that  */
@@ -172,6 +173,39 @@ int32_t paged_attention_workgroups_per_head(int32_t num_seqs, int32_t num_kv_hea
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                        int32_t partition_size);
+
+/* Chunked-prefill attention ([aitalk] the part on the two independent    */
+/* problems: a prompt's K/V are computed in the prefill phase; the part   */
+/* on prefix caching: the prefill of prefixes already seen is skipped, so */
+/* the rest of a prompt attends over cached blocks; step 2: the cache is  */
+/* read through the block table).                                         */
+/*                                                                        */
+/* Sequence s owns query rows query_start[s] .. query_start[s+1]-1: its C */
+/* newest tokens, whose K/V are already in the cache (paged_kv_append),   */
+/* at positions L-C .. L-1 with L = context_lens[s] >= C.  The row of     */
+/* position p and query head h (kv head g = h / G) is                     */
+/*   out[row][h] = sum_{t<=p} softmax_t(scale * <q[row][h], K_t[g]>) V_t[g] */
+/* i.e. causal attention; one-token chunks give the decode result.        */
+/* Scores, softmax and the weighted sum run in fp32 on the matrix cores   */
+/* (bf16 operands: the probabilities enter the value product rounded to   */
+/* bf16); the output is rounded to nearest-even.                          */
+/*                                                                        */
+/* out, q        : device [num_tokens][num_q_heads][head_dim], bf16 only  */
+/*                 (PKV_ERR_UNSUPPORTED otherwise); rows of a sequence    */
+/*                 are contiguous, sequences in order                     */
+/* query_start   : device int32 [num_seqs + 1], rising from 0 to          */
+/*                 num_tokens; every chunk length <= max_query_len        */
+/* max_query_len : host bound on the chunk lengths (sizes the launch)     */
+/* block_tables, context_lens, pools: as for paged_attention_decode       */
+/* scale         : > 0 (usually 1/sqrt(head_dim))                         */
+/* Query group sizes up to 128 are supported.  No workspace; the kernel   */
+/* clamps lengths, offsets and block ids to the given sizes, so bad       */
+/* device values give wrong rows, never accesses outside the buffers.    */
+int32_t paged_attention_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                                int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                int32_t max_query_len, float scale, pkv_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------ */
 /* Host block manager ([pl] Komponenty: block table, block manager with a */

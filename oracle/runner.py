@@ -106,6 +106,13 @@ class OracleRun:
         self.step_done = k
         return out
 
+    def prefill_step(self, k):
+        """Prefill step ``k``: append each sequence's chunk; returns (slots, pairs)."""
+        sids = self.w.decode_seqs
+        out = self._append(sids, list(self.w.chunk_lens), ("chunk", k))
+        self.step_done = k
+        return out
+
     # ------------------------------------------------------------ views
     def tables(self, max_blocks=None):
         sids = self.w.decode_seqs
@@ -118,6 +125,27 @@ class OracleRun:
         """Oracle decode over the materialised pools, fp64 ``[S][H_q][d]``."""
         tables, lens = self.tables()
         return _att.decode_attention(_storage(q), self.k_pool, self.v_pool, tables, lens, scale)
+
+    def prefill_attention(self, q, scale=None):
+        """Oracle chunked-prefill attention over the materialised pools, fp64 ``[T][H_q][d]``."""
+        tables, lens = self.tables()
+        return _att.prefill_attention(_storage(q), self.k_pool, self.v_pool, tables, lens, self.w.query_start(), scale)
+
+    def logical_prefill_row(self, q, row, scale=None, abs_v=False):
+        """Oracle attention of one chunk row from its sequence's logical tokens
+        (positions 0..p); with ``abs_v`` the same weights applied to |V|."""
+        qs = self.w.query_start()
+        s = int(np.searchsorted(qs, row, side="right")) - 1
+        sid = self.w.decode_seqs[s]
+        L = len(self.sources[sid])
+        p = L - int(qs[s + 1] - qs[s]) + (row - int(qs[s]))
+        k, v = self.logical_kv(sid)
+        qrow = _pool.to_f64(_storage(q[row]))
+        if scale is None:
+            scale = 1.0 / np.sqrt(qrow.shape[-1])
+        if abs_v:
+            v = np.abs(v)
+        return _att.dense_attention(qrow, k[: p + 1], v[: p + 1], scale)
 
     def logical_kv(self, sid):
         """fp64 K, V ``[L][H_kv][d]`` of one sequence, rebuilt from its token sources."""

@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     block_digest,
     new_pools,
     paged_attention_decode,
+    paged_attention_prefill,
     paged_attention_workgroups_per_head,
     paged_attention_workspace_bytes,
     paged_kv_append,

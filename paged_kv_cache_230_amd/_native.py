@@ -70,6 +70,9 @@ _SIGS = {
     ),
     "paged_attention_workgroups_per_head": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "paged_attention_prefill": (
+        _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+               _vp]),
     "pkv_bm_create": (_i32, [_i32, _i32, _pi32, C.POINTER(_vp)]),
     "pkv_bm_destroy": (None, [_vp]),
     "pkv_bm_add_seq": (_i32, [_vp, _i64]),

@@ -166,6 +166,38 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
+def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len,
+                            scale=None):
+    """Causal chunked-prefill attention over the paged cache (bf16).
+
+    ``q``/``out``: ``[T][H_q][d]`` with sequence s owning rows
+    ``query_start[s] .. query_start[s+1]-1`` (its newest tokens, already
+    appended); ``query_start``: int32 ``[S+1]`` on the device;
+    ``max_query_len``: host bound on the chunk lengths."""
+    dev = q.device
+    T, Hq, d = q.shape
+    nb, H, _, bs, _ = k_cache.shape
+    S = context_lens.shape[0]
+    _need(q, "q", k_cache.dtype, dev)
+    _need(out, "out", k_cache.dtype, dev)
+    for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"), (query_start, "query_start")):
+        _need(t, name, torch.int32, dev)
+    if tuple(out.shape) != (T, Hq, d):
+        raise ValueError("out must have the shape of q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(query_start.shape) != (S + 1,):
+        raise ValueError("block_tables must be [S][max_blocks] and query_start [S+1]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    N.check(
+        N.lib.paged_attention_prefill(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+            _ptr(query_start), S, T, Hq, H, d, bs, nb, block_tables.shape[1], int(max_query_len), float(scale),
+            _dt(k_cache.dtype), _stream(dev),
+        )
+    )
+    return out
+
+
 def _i64p(a: np.ndarray):
     return a.ctypes.data_as(C.POINTER(C.c_int64))
 

@@ -81,6 +81,40 @@ def product_step(cache, w, k, partition_size=0):
     return out, slots, pairs
 
 
+# Prefill: the probabilities enter the bf16 value product rounded to bf16
+# (unit roundoff u = 2^-8) while the normaliser sums them unrounded in fp32,
+# so each output element is off by at most u * A, A = the softmax-weighted
+# mean of |V| (the oracle run on |V|), plus u * |out| for rounding the output
+# to bf16; 1e-5 * A covers the fp32 accumulation.
+BF16_U = 2.0 ** -8
+
+
+def assert_within_prefill_bound(got, ref, absv, what=""):
+    g = got.float().cpu().double().numpy() if hasattr(got, "cpu") else np.asarray(got, np.float64)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    bound = BF16_U * (absv + np.abs(ref)) + 1e-5 * absv + 1e-7
+    worst = float((err / bound).max())
+    say(f"  {what}: max abs {err.max():.3e}, max err/bound {worst:.3f}")
+    assert err.max() <= TOL["bf16"]["abs"], f"{what}: max abs error {err.max()} > {TOL['bf16']['abs']}"
+    assert worst <= 1.0, f"{what}: error exceeds the bf16-probability bound by {worst:.3f}x"
+
+
+def product_prefill_step(cache, w, k):
+    """Prefill step k through the library: append every chunk, then causal attention."""
+    from paged_kv_cache_230_amd import paged_attention_prefill
+
+    kn, vn = w.kv(("chunk", k))
+    slots, pairs = cache.append(w.decode_seqs, w.chunk_lens, kn, vn)
+    q = w.prefill_q(k).to(cache.device)
+    tables, lens, _, _ = cache.tables(w.decode_seqs)
+    qs = torch.from_numpy(w.query_start().astype(np.int32)).to(cache.device)
+    out = torch.full_like(q, float("nan"))
+    paged_attention_prefill(out, q, cache.k_cache, cache.v_cache, tables, lens, qs, max(w.chunk_lens))
+    torch.cuda.synchronize()
+    return out, slots, pairs
+
+
 def assert_pools_equal(cache, run):
     kg, vg = storage_np(cache.k_cache), storage_np(cache.v_cache)
     assert kg.shape == run.k_pool.shape and vg.shape == run.v_pool.shape

@@ -33,6 +33,11 @@ The five workloads follow the configurations the task is measured on:
   tenants with their own salts; 2 earlier requests (one per tenant) are
   admitted and released first, so the 50 find the system prompt's blocks
   on the eviction list.  8B-shaped heads, block 16, 20k-block pool.
+* ``c7_prefill_bf16`` -- chunked prefill: 16 sequences of the 70B-shaped
+  layer, each with a cached history of uniform [0, 8192] tokens; every
+  step appends a chunk of uniform [128, 1024] new tokens per sequence (the
+  same length each step) and runs causal attention of the chunk over the
+  whole cache.  Block 16, 48k-block pool.
 
 Reading of the length convention: a stated context length is the number of
 tokens the decode attention reads *including* the token appended in that
@@ -53,7 +58,11 @@ Script operations (tuples):
 After the setup script, each of ``steps`` decode steps appends one token to
 every sequence of ``decode_seqs`` (values ``kv(("step", k))``) and then
 runs decode attention with queries ``q(k)``; ``step_tokens(k)`` gives the
-new tokens' ids where the workload tracks them (else None).
+new tokens' ids where the workload tracks them (else None).  A prefill
+workload's step instead appends ``chunk_lens[i]`` tokens to each sequence
+(values ``kv(("chunk", k))``, sequence-major) and runs causal attention of
+those tokens with queries ``prefill_q(k)`` (rows packed by sequence,
+offsets ``query_start()``).
 """
 from __future__ import annotations
 
@@ -94,6 +103,7 @@ CONFIGS = {
     "c4_prefix_bf16": Config("c4_prefix_bf16", "bf16", 32, 8, 128, 16, 128 ** -0.5, 234),
     "c5_mixed_bs32_bf16": Config("c5_mixed_bs32_bf16", "bf16", 64, 8, 128, 32, 128 ** -0.5, 235, steps=10),
     "c6_prefix_cache_bf16": Config("c6_prefix_cache_bf16", "bf16", 32, 8, 128, 16, 128 ** -0.5, 236),
+    "c7_prefill_bf16": Config("c7_prefill_bf16", "bf16", 64, 8, 128, 16, 128 ** -0.5, 237),
 }
 
 # Stress variants of the value distribution (same shapes).  With the
@@ -104,7 +114,7 @@ CONFIGS = {
 VARIANTS = ("plain", "q64", "q512", "needle", "large")
 
 _KEY_TAGS = {"prefill": 1, "step": 2, "q": 3, "prefix": 4, "suffix": 5, "needle": 6, "system": 7, "user": 8,
-             "system_tokens": 9, "user_tokens": 10, "step_tokens": 11}
+             "system_tokens": 9, "user_tokens": 10, "step_tokens": 11, "chunk": 12, "chunk_q": 13}
 VOCAB = 32000
 
 
@@ -149,6 +159,7 @@ class Workload:
             "c4_prefix_bf16": self._build_prefix,
             "c5_mixed_bs32_bf16": self._build_plain_c5,
             "c6_prefix_cache_bf16": self._build_cached,
+            "c7_prefill_bf16": self._build_prefill,
         }[self.name]
         builder(rng)
 
@@ -256,6 +267,38 @@ class Workload:
                                 dtype=np.int64)
         self.tracks_tokens = True
 
+    def _build_prefill(self, rng):
+        """Histories in the cache, then chunks of new tokens every step."""
+        o = self.overrides
+        S = int(o.get("num_seqs", 16))
+        hist = rng.integers(0, int(o.get("history_max", 8192)) + 1, size=S).astype(np.int64)
+        chunks = rng.integers(int(o.get("chunk_min", 128)), int(o.get("chunk_max", 1024)) + 1, size=S)
+        if "histories" in o:
+            hist = np.asarray(o["histories"], dtype=np.int64)
+        if "chunks" in o:
+            chunks = np.asarray(o["chunks"], dtype=np.int64)
+        self.num_blocks = int(o.get("num_blocks", 48000))
+        self.free_order = rng.permutation(self.num_blocks).astype(np.int32)
+        self.chunk_lens = [int(c) for c in chunks]
+        self.decode_seqs = list(range(len(hist)))
+        ops = [("add", s) for s in self.decode_seqs]
+        for s, h in enumerate(hist):
+            if h > 0:
+                ops.append(("append", [s], [int(h)], ("prefill", s)))
+        self.setup_ops = ops
+        self.prefill_rows = {s: int(h) for s, h in enumerate(hist)}
+        self.lengths = (hist + chunks).astype(np.int64)  # context of the first step's chunks
+
+    def query_start(self):
+        """Row offsets of the sequences' chunks in ``prefill_q`` (int64 ``[S+1]``)."""
+        return np.concatenate([[0], np.cumsum(self.chunk_lens)]).astype(np.int64)
+
+    def prefill_q(self, step: int):
+        """Queries of step ``step``'s chunks ``[sum(chunk_lens)][num_q_heads][head_dim]``."""
+        c = self.config
+        shape = (int(sum(self.chunk_lens)), c.num_q_heads, c.head_dim)
+        return self._randn(("chunk_q", step), shape, c.value_std * self._q_scale()).to(c.torch_dtype)
+
     def _ints(self, key, n):
         g = torch.Generator().manual_seed(_key_seed(self.config.seed, key))
         return torch.randint(0, VOCAB, (n,), generator=g, dtype=torch.int64).numpy()
@@ -307,6 +350,8 @@ class Workload:
             ks, vs = self.kv(("system",))
             ku, vu = self.kv(("user", int(key[1])))
             return torch.cat([ks, ku]), torch.cat([vs, vu])
+        elif key[0] == "chunk":
+            T = int(sum(self.chunk_lens))
         elif key[0] == "system":
             T = self.prefix_len
         elif key[0] == "user":
