@@ -35,7 +35,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "decode attention KV GB/s (% of HBM peak) and tokens/s, 70B-shaped layer @32k"
+PREFILL_METRIC = "chunked-prefill attention TFLOP/s (causal, 70B-shaped layer)"
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
+MFMA_BF16_PEAK = 2.5e15  # MI355X dense bf16 matrix-core flop/s
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_230_amd", "csrc", "pagedkv_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c3_traffic.json")
 
@@ -57,6 +59,17 @@ def decode_kv_bytes(lens, num_kv_heads, head_dim, elem_bytes):
 
 def decode_flops(lens, num_q_heads, head_dim):
     return sum(4 * num_q_heads * head_dim * int(L) for L in lens)
+
+
+def prefill_flops(lens, chunks, num_q_heads, head_dim):
+    """Causal work of one prefill call: the token at position p attends to
+    p + 1 keys, 4 * H_q * d flops per key (Q K^T and P V, multiply + add)."""
+    f = 0
+    for L, C in zip(lens, chunks):
+        L, C = int(L), int(C)
+        keys = C * (L - C) + C * (C + 1) // 2  # sum over p = L-C .. L-1 of (p + 1)
+        f += 4 * num_q_heads * head_dim * keys
+    return f
 
 
 def kernel_source_sha() -> str:
@@ -167,6 +180,153 @@ def cpu_baseline(workload_name, num_seqs):
     }
 
 
+# ------------------------------------------------------------ prefill leg
+def run_prefill(args, w, dev):
+    """Consecutive chunked-prefill steps: each appends every sequence's chunk
+    (bookkeeping, slot upload, append kernel) and runs causal attention of
+    the chunk over the whole cache."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_230_amd as pkv
+
+    c = w.config
+    S = w.num_seqs
+    nsteps = args.warmup + args.steps
+    cache = pkv.PagedKVCache(w.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.torch_dtype, dev,
+                             w.free_order)
+    for op in w.setup_ops:
+        cache.apply(op, w.kv)
+    # Two distinct sets of chunk values, alternated (values do not steer the kernels).
+    kvq = []
+    for k in range(2):
+        kn, vn = w.kv(("chunk", k))
+        kvq.append((kn.to(dev), vn.to(dev), w.prefill_q(k).to(dev)))
+    T = int(sum(w.chunk_lens))
+    out = torch.empty(T, c.num_q_heads, c.head_dim, dtype=c.torch_dtype, device=dev)
+    qs = torch.from_numpy(w.query_start().astype(np.int32)).to(dev)
+    seqs = list(w.decode_seqs)
+    bs = c.block_size
+    max_len = max(cache.bm.seq_len(s) for s in seqs) + nsteps * max(w.chunk_lens)
+    max_blocks = -(-max_len // bs)
+    tables_h = torch.empty(S, max_blocks, dtype=torch.int32, pin_memory=True)
+    lens_h = torch.empty(S, dtype=torch.int32, pin_memory=True)
+    slots_h = torch.empty(T, dtype=torch.int32, pin_memory=True)
+    tables_d = torch.empty(S, max_blocks, dtype=torch.int32, device=dev)
+    lens_d = torch.empty(S, dtype=torch.int32, device=dev)
+    slots_d = torch.empty(T, dtype=torch.int32, device=dev)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
+    done = [torch.cuda.Event() for _ in range(nsteps)]
+    step_lens = []
+
+    def step(k):
+        if k:
+            done[k - 1].synchronize()  # the pinned staging buffers are free again
+        slots, pairs = cache.bm.append_slots(seqs, w.chunk_lens)
+        assert pairs.shape[0] == 0
+        slots_h.numpy()[:] = slots
+        cache.bm.block_tables(seqs, max_blocks, tables_h.numpy(), lens_h.numpy())
+        step_lens.append(lens_h.numpy().copy())
+        slots_d.copy_(slots_h, non_blocking=True)
+        tables_d.copy_(tables_h, non_blocking=True)
+        lens_d.copy_(lens_h, non_blocking=True)
+        kn, vn, q = kvq[k % 2]
+        pkv.paged_kv_append(kn, vn, cache.k_cache, cache.v_cache, slots_d)
+        ev0[k].record()
+        pkv.paged_attention_prefill(out, q, cache.k_cache, cache.v_cache, tables_d, lens_d, qs, max(w.chunk_lens))
+        ev1[k].record()
+        done[k].record()
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} prefill steps)", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for k in range(args.warmup, nsteps):
+        step(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timed = range(args.warmup, nsteps)
+    call_s = [ev0[k].elapsed_time(ev1[k]) / 1e3 for k in timed]
+    flops = [prefill_flops(step_lens[k], w.chunk_lens, c.num_q_heads, c.head_dim) for k in timed]
+    achieved = sum(flops) / sum(call_s)
+    value = sum(flops) / elapsed
+    return {
+        "metric": PREFILL_METRIC,
+        "value": round(value / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_seqs": S,
+            "chunk_tokens_per_step": T,
+            "context_first_step": [int(min(step_lens[args.warmup])), int(max(step_lens[args.warmup]))],
+            "context_last_step": [int(min(step_lens[-1])), int(max(step_lens[-1]))],
+            "num_q_heads": c.num_q_heads,
+            "num_kv_heads": c.num_kv_heads,
+            "head_dim": c.head_dim,
+            "block_size": bs,
+        },
+        "tokens_per_s": round(T * args.steps / elapsed, 1),
+        "prefill_call_ms": round(1e3 * sum(call_s) / len(call_s), 4),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "paged_attention_prefill",
+            "achieved": round(achieved / 1e12, 2),
+            "peak": MFMA_BF16_PEAK / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK, 4),
+            "traffic": None,
+            "algorithmic_flops_per_call_mean": int(sum(flops) / len(flops)),
+        },
+        "cpu_baseline": None,
+    }
+
+
+def prefill_cpu_baseline(w, num_seqs):
+    """The oracle's prefill attention timed on the host over a bounded
+    sample: the first ``num_seqs`` sequences of the workload (their history
+    and chunk lengths; pool materialised before timing), scaled to TFLOP/s
+    with the same causal flop count."""
+    from threadpoolctl import threadpool_info
+
+    from oracle.runner import OracleRun
+    from workloads import Workload
+
+    n = num_seqs or 2
+    c = w.config
+    hist = [int(L) - int(C) for L, C in zip(w.lengths[:n], w.chunk_lens[:n])]
+    chunks = [int(C) for C in w.chunk_lens[:n]]
+    need = sum(-(-int(L) // c.block_size) for L in w.lengths[:n])
+    ws = Workload(w.name, overrides=dict(histories=hist, chunks=chunks, num_blocks=need + 8))
+    run = OracleRun(ws)
+    run.prefill_step(0)
+    q = ws.prefill_q(0)
+    t0 = time.perf_counter()
+    run.prefill_attention(q)
+    dt = time.perf_counter() - t0
+    flops = prefill_flops(ws.lengths, chunks, c.num_q_heads, c.head_dim)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "seconds": dt,
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"oracle prefill_attention (fp64) on {n} sequences shaped like the first {n} of the batch: "
+                  f"chunks {chunks}, contexts {[int(L) for L in ws.lengths]}",
+    }
+
+
 # ----------------------------------------------------------------- GPU leg
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -198,6 +358,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = Workload(args.workload)
+    if hasattr(w, "chunk_lens"):
+        result = run_prefill(args, w, dev)
+        if not args.no_cpu_baseline:
+            print("# cpu baseline: oracle on the host", file=sys.stderr, flush=True)
+            result["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_seqs)
+        print(json.dumps(result), flush=True)
+        return
     c = w.config
     S = w.num_seqs
     nsteps = args.warmup + args.steps

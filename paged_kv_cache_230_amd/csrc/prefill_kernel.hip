@@ -25,9 +25,12 @@
 //     columns.  Lane l holds the scores of keys 4(l/16)+i (+16) of row l%16,
 //     which is the B-operand layout of the PV product once its 32 keys are
 //     ordered the same way in A: O^T += V^T P^T, again 16x16x32.
-//   * Online softmax per row in the log2 domain; the causal mask (a select,
-//     never a multiply) only on the steps that reach past the tile's first
-//     position; the accumulators are rescaled only when a running max grows.
+//   * Online softmax per row in the log2 domain; row maxima by gfx950 row
+//     swaps (v_permlane16/32_swap), not LDS shuffles; the causal mask (a
+//     select, never a multiply) only on the steps that reach past the tile's
+//     first position.  A row's reference max moves only when its max grows
+//     by more than 2^8, so the accumulators are rescaled rarely; the
+//     probabilities then stay below 2^8, well inside fp32 and bf16 range.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -65,8 +68,11 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-// One step's K and V: K part [kKeys/BS tiles][D/8][BS][8], then V part
-// [kKeys/BS tiles][D][BS], bf16 — the pool's tile format.
+// One step's K and V in LDS.  K part: [kKeys/BS tiles][D/8][BS][8] bf16,
+// the pool's tile format (the QK A operand is then one contiguous 1 KiB run
+// per wave).  V part: [D][4 lane groups][8] bf16, where group g holds keys
+// 4g..4g+3 and 16+4g..16+4g+3 of the step, the order of the PV product's
+// k index, so each A operand is one 16-byte read.
 template <int D>
 struct StageLayout {
   static constexpr int kBytes = kKeys * D * 2;  // K or V part
@@ -82,11 +88,58 @@ struct PrefillSmem {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// Global loads of step `st` into registers (zeros past the context).
+// Combine the 4 lanes l, l^16, l^32, l^48 (the four 16-lane rows of a
+// wave) with the gfx950 row swaps: v_permlane16_swap(x, y) exchanges the
+// odd rows of x with the even rows of y, v_permlane32_swap the upper half
+// of x with the lower half of y; with y = x, the two results hold every
+// lane's own value and its partner's, in some order.  Each result passes
+// through an empty asm statement before it is combined: the compiler in
+// use otherwise reads the first result twice when one instruction consumes
+// both (it turns max(r0, r1) into r0 and r0 + r1 into r0 + r0).
+__device__ __forceinline__ float opaque_f(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return __builtin_bit_cast(float, v);
+}
+
+template <bool kMax>
+__device__ __forceinline__ float reduce4rows(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float a0 = opaque_f(a[0]), a1 = opaque_f(a[1]);
+  v = kMax ? fmaxf(a0, a1) : a0 + a1;
+  u = __builtin_bit_cast(uint32_t, v);
+  auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float b0 = opaque_f(b[0]), b1 = opaque_f(b[1]);
+  return kMax ? fmaxf(b0, b1) : b0 + b1;
+}
+
+// Where each of a thread's 16-byte staging chunks comes from and goes to;
+// the same every step, only the block ids change.
 template <int D, int BS>
-__device__ __forceinline__ void load_stage(const PrefillArgs& a, int g, int L, const int32_t* table, int st,
-                                           uint4 (&r)[StageLayout<D>::kPerThread]) {
-  constexpr int kTileBytes = BS * D * 2;
+struct StagePlan {
+  static constexpr int kTileBytes = BS * D * 2;
+  int src[StageLayout<D>::kPerThread];   // byte offset inside the (block, kv head) tile
+  int tile[StageLayout<D>::kPerThread];  // tile of the step (0 .. kKeys/BS-1)
+  int dst[StageLayout<D>::kPerThread];   // K: byte offset in the K part; V: first key of the chunk in the step
+  int dim[StageLayout<D>::kPerThread];   // V: the chunk's dim
+  __device__ StagePlan() {
+    // Chunk k of a thread lies in the K part exactly when k < kPerThread / 2
+    // (the K part is the first half of the stage and threads stride it).
+    constexpr int kHalf = StageLayout<D>::kPerThread / 2;
+#pragma unroll
+    for (int k = 0; k < StageLayout<D>::kPerThread; ++k) {
+      const int ov = (threadIdx.x + kPThreads * (k % kHalf)) * 16;
+      tile[k] = ov / kTileBytes;
+      src[k] = ov % kTileBytes;
+      dst[k] = k < kHalf ? ov : tile[k] * BS + (src[k] % (2 * BS)) / 2;  // V: first key of the chunk in the step
+      dim[k] = k < kHalf ? 0 : src[k] / (2 * BS);                        // V tile [D][BS]: 8 keys of one dim
+    }
+  }
+};
+
+template <int D, int BS>
+__device__ __forceinline__ void load_stage(const PrefillArgs& a, const StagePlan<D, BS>& pl, int g, int L,
+                                           const int32_t* table, int st, uint4 (&r)[StageLayout<D>::kPerThread]) {
   constexpr int kTiles = kKeys / BS;
   int32_t ids[kTiles];
 #pragma unroll
@@ -96,37 +149,41 @@ __device__ __forceinline__ void load_stage(const PrefillArgs& a, int g, int L, c
   }
 #pragma unroll
   for (int k = 0; k < StageLayout<D>::kPerThread; ++k) {
-    const int u = threadIdx.x + kPThreads * k;
-    const int o = u * 16;
-    const bool is_v = o >= StageLayout<D>::kBytes;
-    const int ov = is_v ? o - StageLayout<D>::kBytes : o;
-    const int kt = ov / kTileBytes;
-    const int ot = ov % kTileBytes;
-    const int id = ids[kt];
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (id >= 0) {
-      const char* base = static_cast<const char*>(is_v ? a.v_cache : a.k_cache);
-      x = *reinterpret_cast<const uint4*>(base + (static_cast<int64_t>(id) * a.num_kv_heads + g) * kTileBytes + ot);
-      if (is_v) {
-        // V tile [D][BS]: this chunk holds 8 consecutive keys of one dim.
-        const int key0 = (st * kTiles + kt) * BS + (ot % (2 * BS)) / 2;
-        if (key0 + 8 > L) {
-          uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    constexpr int kHalf = StageLayout<D>::kPerThread / 2;  // first half of the chunks is K
+    int id = ids[0];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (key0 + e >= L) w[e / 2] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-          x = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
-    }
-    r[k] = x;
+    for (int kt = 1; kt < kTiles; ++kt) id = pl.tile[k] == kt ? ids[kt] : id;  // select: no dynamic indexing
+    const char* base = static_cast<const char*>(k < kHalf ? a.k_cache : a.v_cache);
+    r[k] = id >= 0 ? *reinterpret_cast<const uint4*>(base + (static_cast<int64_t>(id) * a.num_kv_heads + g) *
+                                                              StagePlan<D, BS>::kTileBytes + pl.src[k])
+                   : make_uint4(0, 0, 0, 0);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_stage(uint4* dst, const uint4 (&r)[StageLayout<D>::kPerThread]) {
+template <int D, int BS>
+__device__ __forceinline__ void store_stage(char* dst, const StagePlan<D, BS>& pl, int key_base, int L,
+                                            uint4 (&r)[StageLayout<D>::kPerThread]) {
+  constexpr int kHalf = StageLayout<D>::kPerThread / 2;
 #pragma unroll
-  for (int k = 0; k < StageLayout<D>::kPerThread; ++k) dst[threadIdx.x + kPThreads * k] = r[k];
+  for (int k = 0; k < kHalf; ++k) *reinterpret_cast<uint4*>(dst + pl.dst[k]) = r[k];
+  char* vdst = dst + StageLayout<D>::kBytes;
+  const bool tail = key_base + kKeys > L;  // uniform: only the step holding the context's end
+#pragma unroll
+  for (int k = kHalf; k < StageLayout<D>::kPerThread; ++k) {
+    uint4 x = r[k];
+    const int kk0 = pl.dst[k];  // first key of the chunk within the step (a multiple of 8)
+    if (tail) {  // zero V slots at or past the context end
+      uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (key_base + kk0 + e >= L) w[e / 2] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      x = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    const int half = kk0 / 16, g0 = (kk0 % 16) / 4;
+    char* row = vdst + pl.dim[k] * 64 + half * 8;
+    *reinterpret_cast<uint2*>(row + g0 * 16) = make_uint2(x.x, x.y);
+    *reinterpret_cast<uint2*>(row + (g0 + 1) * 16) = make_uint2(x.z, x.w);
+  }
 }
 
 template <int D, int BS>
@@ -135,6 +192,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int kTileBytes = BS * D * 2;
   constexpr int kChunks = D / 32;  // 32-dim slices of the QK contraction
   constexpr int kDimTiles = D / 16;
+  // The reference max of a row moves only when the row max exceeds it by
+  // more than this (log2 units), so probabilities stay below 2^8 and the
+  // accumulators are rescaled only on such moves.
+  constexpr float kSlack = 8.f;
   const int s = blockIdx.z;
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -160,6 +221,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int mask_from = (pos0 + 1) / kKeys;  // steps before this one see no key past pos0
   const int G = a.group;
   const int32_t* table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+  const StagePlan<D, BS> plan;
 
   // This lane's two rows (one per row set): token, head, position, validity.
   int row_pos[kRowSets];
@@ -197,13 +259,13 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 
   uint4 nxt[StageLayout<D>::kPerThread];
-  load_stage<D, BS>(a, g, L, table, 0, nxt);
-  store_stage<D>(sm.stage[0], nxt);
+  load_stage<D, BS>(a, plan, g, L, table, 0, nxt);
+  store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[0]), plan, 0, L, nxt);
   __syncthreads();
 
   for (int st = 0; st < nsteps; ++st) {
     const bool more = st + 1 < nsteps;
-    if (more) load_stage<D, BS>(a, g, L, table, st + 1, nxt);
+    if (more) load_stage<D, BS>(a, plan, g, L, table, st + 1, nxt);
     const char* kl = reinterpret_cast<const char*>(sm.stage[st & 1]);
     const char* vl = kl + StageLayout<D>::kBytes;
 
@@ -228,78 +290,64 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     const bool masked = st >= mask_from;
     bf16x8 pb[kRowSets];
     float alpha[kRowSets];
-    bool grew = false;
+    bool moved = false;
 #pragma unroll
     for (int rs = 0; rs < kRowSets; ++rs) {
       float x[8];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sc[rs][h][i];
-          if (masked) {
-            const int key = st * kKeys + h * 16 + grp * 4 + i;
-            v = key <= row_pos[rs] ? v : -INFINITY;
-          }
-          x[h * 4 + i] = v;
-        }
-      float mx = x[0];
+        for (int i = 0; i < 4; ++i) x[h * 4 + i] = sc[rs][h][i];
+      if (masked) {
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[rs], mx * a.scale_log2);
-      alpha[rs] = exp2f(m_run[rs] - m_new);
-      grew |= m_new > m_run[rs];
-      m_run[rs] = m_new;
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (st * kKeys + h * 16 + grp * 4 + i > row_pos[rs]) x[h * 4 + i] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mx = reduce4rows<true>(mx) * a.scale_log2;
+      const bool move = mx > m_run[rs] + kSlack;
+      const float m_use = move ? mx : m_run[rs];
+      alpha[rs] = __builtin_amdgcn_exp2f(m_run[rs] - m_use);
+      moved |= move;
+      m_run[rs] = m_use;
       float sum = 0.f;
       __bf16 pe[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(fmaf(x[e], a.scale_log2, -m_new));
+        const float p = __builtin_amdgcn_exp2f(fmaf(x[e], a.scale_log2, -m_use));
         sum += p;
         pe[e] = static_cast<__bf16>(p);
       }
       l_run[rs] = l_run[rs] * alpha[rs] + sum;
       pb[rs] = bf16x8{pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]};
     }
-    if (__builtin_amdgcn_ballot_w64(grew)) {
+    if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
       for (int rs = 0; rs < kRowSets; ++rs)
 #pragma unroll
         for (int t = 0; t < kDimTiles; ++t) acc[rs][t] *= alpha[rs];
     }
 
-    // ---- O^T += V^T P^T.  MFMA k index 8*grp+e is key 4*grp+e (e < 4) of
-    // the first half and 16+4*grp+(e-4) of the second, as in pb.
+    // ---- O^T += V^T P^T: A = V^T rows dim 16t+col, k index 8*grp+e = the
+    // keys of lane group grp in the interleaved V layout.
 #pragma unroll
     for (int t = 0; t < kDimTiles; ++t) {
-      const int dim = t * 16 + col;
-      uint2 lo, hi;
-      {
-        const int kk = grp * 4, kt = kk / BS, kb = kk % BS;
-        lo = *reinterpret_cast<const uint2*>(vl + kt * kTileBytes + (dim * BS + kb) * 2);
-      }
-      {
-        const int kk = 16 + grp * 4, kt = kk / BS, kb = kk % BS;
-        hi = *reinterpret_cast<const uint2*>(vl + kt * kTileBytes + (dim * BS + kb) * 2);
-      }
-      const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(vl + (t * 16 + col) * 64 + grp * 16);
 #pragma unroll
       for (int rs = 0; rs < kRowSets; ++rs)
         acc[rs][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rs], acc[rs][t], 0, 0, 0);
     }
 
-    if (more) store_stage<D>(sm.stage[(st + 1) & 1], nxt);
+    if (more) store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[(st + 1) & 1]), plan, (st + 1) * kKeys, L, nxt);
     __syncthreads();
   }
 
   // ---- normalise and store: lane holds dims 16t + 4*grp + i of row col.
 #pragma unroll
   for (int rs = 0; rs < kRowSets; ++rs) {
-    float l = l_run[rs];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = reduce4rows<false>(l_run[rs]);
     if (!row_ok[rs]) continue;
     const float inv = 1.f / l;
     __bf16* orow = static_cast<__bf16*>(a.out) + row_q[rs];
