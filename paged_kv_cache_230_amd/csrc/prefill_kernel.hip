@@ -13,18 +13,19 @@
 //   * One workgroup = 4 waves = one (query tile, kv head, sequence).  The
 //     128 score rows of a tile are (query token, query head) pairs of the
 //     G heads sharing the kv head, so every K/V byte staged serves G heads.
-//     Wave w owns rows 32w..32w+31 as two 16-row sets.
+//     Wave w owns rows 32w..32w+31, one per lane pair (l, l+32).
 //   * Keys advance 32 per step.  The step's K and V block tiles are copied
 //     into LDS in the pool's own format (double-buffered: the next step's
 //     global loads are in flight during this step's matrix work); block ids
 //     come from uniform (scalar) loads.  V slots past the context are
 //     zeroed in LDS, so unused slots of the last block never reach the
 //     products.
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: keys in the A operand (one
-//     16-byte LDS read per lane serves both row sets), query rows in the
-//     columns.  Lane l holds the scores of keys 4(l/16)+i (+16) of row l%16,
-//     which is the B-operand layout of the PV product once its 32 keys are
-//     ordered the same way in A: O^T += V^T P^T, again 16x16x32.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the step's 32 keys in the
+//     rows, the wave's 32 query rows in the columns.  Lane l holds 16
+//     scores of row l%32 (keys 8(j/4)+4(l/32)+j%4), so a row's max needs one
+//     partner lane.  Those scores, in that order, are the B operand of the
+//     PV product once A (V^T, read from LDS) orders its k index the same
+//     way: O^T += V^T P^T, again 32x32x16.
 //   * Online softmax per row in the log2 domain; row maxima by gfx950 row
 //     swaps (v_permlane16/32_swap), not LDS shuffles; the causal mask (a
 //     select, never a multiply) only on the steps that reach past the tile's
@@ -41,13 +42,15 @@
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float float4v;
+typedef __attribute__((ext_vector_type(16))) float float16v;
 
 constexpr int kPWaves = 4;
 constexpr int kPThreads = 64 * kPWaves;
-constexpr int kRowSets = 2;                   // 16-row sets per wave
-constexpr int kRows = kPWaves * kRowSets * 16;  // score rows per workgroup
+constexpr int kRows = kPWaves * 32;  // score rows per workgroup (32 per wave)
 constexpr int kKeys = 32;                     // keys per step
+// Block ids of the tile's key range are staged in LDS this many at a time
+// (a vector load of a table entry per step would stall its wave).
+constexpr int kIdChunk = 1024;
 
 struct PrefillArgs {
   void* out;
@@ -69,45 +72,45 @@ struct PrefillArgs {
 };
 
 // One step's K and V in LDS.  K part: [kKeys/BS tiles][D/8][BS][8] bf16,
-// the pool's tile format (the QK A operand is then one contiguous 1 KiB run
-// per wave).  V part: [D][4 lane groups][8] bf16, where group g holds keys
-// 4g..4g+3 and 16+4g..16+4g+3 of the step, the order of the PV product's
-// k index, so each A operand is one 16-byte read.
+// the pool's tile format (each 16-lane quarter of a QK A operand read is a
+// contiguous 256-byte run).  V part: [D][4 groups][8] bf16, group 2m+h
+// holding keys 16m+4h+{0..3} then 16m+8+4h+{0..3}: the k order of PV
+// product m for lanes with l/32 = h, so each A operand is one 16-byte read;
+// rows are padded from 64 to 80 bytes so the 16 dims a quarter-wave reads
+// fall in distinct banks.
+constexpr int kVRow = 80;  // bytes per dim row of the V part
 template <int D>
 struct StageLayout {
-  static constexpr int kBytes = kKeys * D * 2;  // K or V part
-  static constexpr int kUint4 = 2 * kBytes / 16;
-  static constexpr int kPerThread = kUint4 / kPThreads;
-  static_assert(kUint4 % kPThreads == 0, "stage must split evenly over the threads");
+  static constexpr int kBytes = kKeys * D * 2;  // data bytes of the K or the V part
+  static constexpr int kVBytes = D * kVRow;     // V part with padding
+  static constexpr int kStageBytes = kBytes + kVBytes;
+  static constexpr int kPerThread = 2 * kBytes / 16 / kPThreads;  // 16-byte chunks per thread
+  static_assert((2 * kBytes / 16) % kPThreads == 0, "stage must split evenly over the threads");
 };
 
 template <int D>
 struct PrefillSmem {
-  uint4 stage[2][StageLayout<D>::kUint4];
+  uint4 stage[2][StageLayout<D>::kStageBytes / 16];
+  int32_t ids[kIdChunk];
 };
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// Combine the 4 lanes l, l^16, l^32, l^48 (the four 16-lane rows of a
-// wave) with the gfx950 row swaps: v_permlane16_swap(x, y) exchanges the
-// odd rows of x with the even rows of y, v_permlane32_swap the upper half
-// of x with the lower half of y; with y = x, the two results hold every
-// lane's own value and its partner's, in some order.  Each result passes
-// through an empty asm statement before it is combined: the compiler in
-// use otherwise reads the first result twice when one instruction consumes
-// both (it turns max(r0, r1) into r0 and r0 + r1 into r0 + r0).
+// Combine lanes l and l^32 (the two holders of a score row) with the
+// gfx950 swap v_permlane32_swap(x, y), which exchanges the upper half of x
+// with the lower half of y: with y = x its two results hold every lane's
+// own value and its partner's, in some order.  Each result passes through an
+// empty asm statement before they are combined: the compiler in use
+// otherwise reads the first result twice when one instruction consumes both
+// (max(r0, r1) becomes r0, r0 + r1 becomes r0 + r0).
 __device__ __forceinline__ float opaque_f(uint32_t v) {
   asm volatile("" : "+v"(v));
   return __builtin_bit_cast(float, v);
 }
 
 template <bool kMax>
-__device__ __forceinline__ float reduce4rows(float v) {
-  uint32_t u = __builtin_bit_cast(uint32_t, v);
-  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float a0 = opaque_f(a[0]), a1 = opaque_f(a[1]);
-  v = kMax ? fmaxf(a0, a1) : a0 + a1;
-  u = __builtin_bit_cast(uint32_t, v);
+__device__ __forceinline__ float reduce_pair(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
   auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   const float b0 = opaque_f(b[0]), b1 = opaque_f(b[1]);
   return kMax ? fmaxf(b0, b1) : b0 + b1;
@@ -118,11 +121,12 @@ __device__ __forceinline__ float reduce4rows(float v) {
 template <int D, int BS>
 struct StagePlan {
   static constexpr int kTileBytes = BS * D * 2;
+  const char* base[StageLayout<D>::kPerThread];  // pool + kv head tile + src (add id * stride)
   int src[StageLayout<D>::kPerThread];   // byte offset inside the (block, kv head) tile
   int tile[StageLayout<D>::kPerThread];  // tile of the step (0 .. kKeys/BS-1)
   int dst[StageLayout<D>::kPerThread];   // K: byte offset in the K part; V: first key of the chunk in the step
   int dim[StageLayout<D>::kPerThread];   // V: the chunk's dim
-  __device__ StagePlan() {
+  __device__ StagePlan(const PrefillArgs& a, int g) {
     // Chunk k of a thread lies in the K part exactly when k < kPerThread / 2
     // (the K part is the first half of the stage and threads stride it).
     constexpr int kHalf = StageLayout<D>::kPerThread / 2;
@@ -133,30 +137,34 @@ struct StagePlan {
       src[k] = ov % kTileBytes;
       dst[k] = k < kHalf ? ov : tile[k] * BS + (src[k] % (2 * BS)) / 2;  // V: first key of the chunk in the step
       dim[k] = k < kHalf ? 0 : src[k] / (2 * BS);                        // V tile [D][BS]: 8 keys of one dim
+      base[k] = static_cast<const char*>(k < kHalf ? a.k_cache : a.v_cache) + g * kTileBytes + src[k];
     }
   }
 };
 
-template <int D, int BS>
-__device__ __forceinline__ void load_stage(const PrefillArgs& a, const StagePlan<D, BS>& pl, int g, int L,
-                                           const int32_t* table, int st, uint4 (&r)[StageLayout<D>::kPerThread]) {
-  constexpr int kTiles = kKeys / BS;
-  int32_t ids[kTiles];
-#pragma unroll
-  for (int kt = 0; kt < kTiles; ++kt) {
-    const int lb = st * kTiles + kt;
-    ids[kt] = lb * BS < L ? clampi(table[lb], 0, a.num_blocks - 1) : -1;
+// Staged block ids [chunk_base, chunk_base + kIdChunk) of the sequence,
+// clamped to the pool; -1 past the context.
+__device__ __forceinline__ void fill_ids(const PrefillArgs& a, const int32_t* table, int chunk_base, int nblk,
+                                         int32_t* ids) {
+  for (int i = threadIdx.x; i < kIdChunk; i += kPThreads) {
+    const int lb = chunk_base + i;
+    ids[i] = lb < nblk ? clampi(table[lb], 0, a.num_blocks - 1) : -1;
   }
+}
+
+template <int D, int BS>
+__device__ __forceinline__ void load_stage(const StagePlan<D, BS>& pl, int64_t stride, const int32_t* ids,
+                                           int first, uint4 (&r)[StageLayout<D>::kPerThread]) {
+  constexpr int kTiles = kKeys / BS;
+  int32_t id[kTiles];
+#pragma unroll
+  for (int kt = 0; kt < kTiles; ++kt) id[kt] = ids[first + kt];  // uniform LDS reads
 #pragma unroll
   for (int k = 0; k < StageLayout<D>::kPerThread; ++k) {
-    constexpr int kHalf = StageLayout<D>::kPerThread / 2;  // first half of the chunks is K
-    int id = ids[0];
+    int b = id[0];
 #pragma unroll
-    for (int kt = 1; kt < kTiles; ++kt) id = pl.tile[k] == kt ? ids[kt] : id;  // select: no dynamic indexing
-    const char* base = static_cast<const char*>(k < kHalf ? a.k_cache : a.v_cache);
-    r[k] = id >= 0 ? *reinterpret_cast<const uint4*>(base + (static_cast<int64_t>(id) * a.num_kv_heads + g) *
-                                                              StagePlan<D, BS>::kTileBytes + pl.src[k])
-                   : make_uint4(0, 0, 0, 0);
+    for (int kt = 1; kt < kTiles; ++kt) b = pl.tile[k] == kt ? id[kt] : b;  // select: no dynamic indexing
+    r[k] = b >= 0 ? *reinterpret_cast<const uint4*>(pl.base[k] + b * stride) : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -179,10 +187,12 @@ __device__ __forceinline__ void store_stage(char* dst, const StagePlan<D, BS>& p
         if (key_base + kk0 + e >= L) w[e / 2] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
       x = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    const int half = kk0 / 16, g0 = (kk0 % 16) / 4;
-    char* row = vdst + pl.dim[k] * 64 + half * 8;
-    *reinterpret_cast<uint2*>(row + g0 * 16) = make_uint2(x.x, x.y);
-    *reinterpret_cast<uint2*>(row + (g0 + 1) * 16) = make_uint2(x.z, x.w);
+    // keys kk0..kk0+3 go to group 2m, kk0+4..kk0+7 to group 2m+1, each at
+    // element (kk0 % 16) / 8 * 4 of its group (m = kk0 / 16).
+    const int m = kk0 / 16;
+    char* row = vdst + pl.dim[k] * kVRow + ((kk0 % 16) / 8) * 8;
+    *reinterpret_cast<uint2*>(row + (2 * m) * 16) = make_uint2(x.x, x.y);
+    *reinterpret_cast<uint2*>(row + (2 * m + 1) * 16) = make_uint2(x.z, x.w);
   }
 }
 
@@ -190,8 +200,6 @@ template <int D, int BS>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillSmem<D> sm;
   constexpr int kTileBytes = BS * D * 2;
-  constexpr int kChunks = D / 32;  // 32-dim slices of the QK contraction
-  constexpr int kDimTiles = D / 16;
   // The reference max of a row moves only when the row max exceeds it by
   // more than this (log2 units), so probabilities stay below 2^8 and the
   // accumulators are rescaled only on such moves.
@@ -200,8 +208,6 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;
-  const int grp = lane >> 4;
 
   const int L = clampi(a.context_lens[s], 0, a.max_blocks_per_seq * BS);
   int q0 = a.query_start[s];
@@ -221,146 +227,150 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int mask_from = (pos0 + 1) / kKeys;  // steps before this one see no key past pos0
   const int G = a.group;
   const int32_t* table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
-  const StagePlan<D, BS> plan;
+  const StagePlan<D, BS> plan(a, g);
+  const int64_t stride = static_cast<int64_t>(a.num_kv_heads) * kTileBytes;  // bytes per pool block
+  constexpr int kTiles = kKeys / BS;
+  const int nblk = (L + BS - 1) / BS;
 
-  // This lane's two rows (one per row set): token, head, position, validity.
-  int row_pos[kRowSets];
-  int64_t row_q[kRowSets];
-  bool row_ok[kRowSets];
-#pragma unroll
-  for (int rs = 0; rs < kRowSets; ++rs) {
-    const int r = wave * (kRowSets * 16) + rs * 16 + col;
+  // This lane's row: token, head, position, validity (lanes l and l+32 share it).
+  const int half = lane >> 5;
+  int row_pos;
+  int64_t row_q;
+  bool row_ok;
+  {
+    const int r = wave * 32 + (lane & 31);
     const int tq = r / G;
     const int j = r - tq * G;
-    row_ok[rs] = tq < ntok;
-    row_pos[rs] = row_ok[rs] ? pos0 + tq : kend - 1;
-    row_q[rs] = row_ok[rs] ? (static_cast<int64_t>(q0 + tok0 + tq) * a.num_q_heads + g * G + j) * D : -1;
+    row_ok = tq < ntok;
+    row_pos = row_ok ? pos0 + tq : kend - 1;
+    row_q = row_ok ? (static_cast<int64_t>(q0 + tok0 + tq) * a.num_q_heads + g * G + j) * D : -1;
   }
 
-  // Queries: B operand of the QK product, lane holds dims 8*grp..+8 of each 32-dim chunk.
-  bf16x8 qb[kRowSets][kChunks];
+  // Queries: B operand of the QK product, lane holds dims 8*half..+8 of each 16-dim chunk.
+  constexpr int kQChunks = D / 16;
+  bf16x8 qb[kQChunks];
 #pragma unroll
-  for (int rs = 0; rs < kRowSets; ++rs)
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (row_ok[rs]) x = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.q) + row_q[rs] + c * 32 + grp * 8);
-      qb[rs][c] = __builtin_bit_cast(bf16x8, x);
-    }
-
-  float4v acc[kRowSets][kDimTiles];
-  float m_run[kRowSets], l_run[kRowSets];
-#pragma unroll
-  for (int rs = 0; rs < kRowSets; ++rs) {
-    m_run[rs] = -INFINITY;
-    l_run[rs] = 0.f;
-#pragma unroll
-    for (int t = 0; t < kDimTiles; ++t) acc[rs][t] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < kQChunks; ++c) {
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (row_ok) x = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.q) + row_q + c * 16 + half * 8);
+    qb[c] = __builtin_bit_cast(bf16x8, x);
   }
 
-  uint4 nxt[StageLayout<D>::kPerThread];
-  load_stage<D, BS>(a, plan, g, L, table, 0, nxt);
-  store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[0]), plan, 0, L, nxt);
+  constexpr int kDimTiles = D / 32;
+  float16v acc[kDimTiles];
+#pragma unroll
+  for (int t = 0; t < kDimTiles; ++t) acc[t] = float16v{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Two register sets carry K/V two steps ahead: step j's chunks live in
+  // set j % 2 from the load issued during step j - 2 until they are written
+  // to LDS at the end of step j - 1.
+  uint4 ra[StageLayout<D>::kPerThread], rb[StageLayout<D>::kPerThread];
+  int chunk_base = 0;
+  fill_ids(a, table, 0, nblk, sm.ids);
+  __syncthreads();
+  load_stage<D, BS>(plan, stride, sm.ids, 0, ra);
+  if (nsteps > 1) load_stage<D, BS>(plan, stride, sm.ids, kTiles, rb);
+  store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[0]), plan, 0, L, ra);
   __syncthreads();
 
-  for (int st = 0; st < nsteps; ++st) {
-    const bool more = st + 1 < nsteps;
-    if (more) load_stage<D, BS>(a, plan, g, L, table, st + 1, nxt);
+  const int key_col = lane & 31;  // key of the QK A operand within the step
+  const int k_tile = key_col / BS, k_in = key_col % BS;
+  auto step = [&](int st, uint4 (&cur)[StageLayout<D>::kPerThread], uint4 (&nxt)[StageLayout<D>::kPerThread]) {
+    // cur: free (step st is in LDS) -> receives step st + 2; nxt: holds step st + 1.
+    if (st + 2 < nsteps) {
+      if ((st + 2) * kTiles >= chunk_base + kIdChunk) {
+        // Every read of the staged ids so far happened before the last barrier.
+        chunk_base += kIdChunk;
+        fill_ids(a, table, chunk_base, nblk, sm.ids);
+        __syncthreads();
+      }
+      load_stage<D, BS>(plan, stride, sm.ids, (st + 2) * kTiles - chunk_base, cur);
+    }
     const char* kl = reinterpret_cast<const char*>(sm.stage[st & 1]);
     const char* vl = kl + StageLayout<D>::kBytes;
 
-    // ---- S^T = K Q^T: two 16-key halves x two row sets.
-    float4v sc[kRowSets][2];
+    // ---- S^T = K Q^T over the step's 32 keys.
+    float16v sc = float16v{};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kk = h * 16 + col;  // key within the step for the A operand
-      const int kt = kk / BS, kb = kk % BS;
+    for (int c = 0; c < kQChunks; ++c) {
+      const bf16x8 ka =
+          *reinterpret_cast<const bf16x8*>(kl + k_tile * kTileBytes + ((c * 2 + half) * BS + k_in) * 16);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[c], sc, 0, 0, 0);
+    }
+
+    // ---- online softmax of this lane's 16 scores (keys 8(j/4)+4*half+j%4).
+    float x[16];  // scores in log2 units
 #pragma unroll
-      for (int rs = 0; rs < kRowSets; ++rs) sc[rs][h] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 16; ++j) x[j] = sc[j] * a.scale_log2;
+    if (st >= mask_from) {
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + kt * kTileBytes + ((c * 4 + grp) * BS + kb) * 16);
+      for (int j = 0; j < 16; ++j)
+        if (st * kKeys + 8 * (j / 4) + 4 * half + (j % 4) > row_pos) x[j] = -INFINITY;
+    }
+    float mx = x[0];
 #pragma unroll
-        for (int rs = 0; rs < kRowSets; ++rs)
-          sc[rs][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[rs][c], sc[rs][h], 0, 0, 0);
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, x[j]);
+    mx = reduce_pair<true>(mx);
+    const bool move = mx > m_run + kSlack;
+    const float m_use = move ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_use;
+    float sum = 0.f;
+    __bf16 pe[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float p = __builtin_amdgcn_exp2f(x[j] - m_use);
+      sum += p;
+      pe[j] = static_cast<__bf16>(p);
+    }
+    l_run = l_run * alpha + sum;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+#pragma unroll
+      for (int t = 0; t < kDimTiles; ++t) acc[t] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T, two products of 16 keys: product m takes this
+    // lane's scores j = 8m..8m+7, i.e. keys 16m+8(i/4)+4*half+i%4, which is
+    // how group 2m+half of the V part orders them.
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 pb = bf16x8{pe[8 * m], pe[8 * m + 1], pe[8 * m + 2], pe[8 * m + 3],
+                               pe[8 * m + 4], pe[8 * m + 5], pe[8 * m + 6], pe[8 * m + 7]};
+#pragma unroll
+      for (int t = 0; t < kDimTiles; ++t) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vl + (t * 32 + key_col) * kVRow + (2 * m + half) * 16);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[t], 0, 0, 0);
       }
     }
 
-    // ---- online softmax per row; P packed as the B operand of the PV product.
-    const bool masked = st >= mask_from;
-    bf16x8 pb[kRowSets];
-    float alpha[kRowSets];
-    bool moved = false;
-#pragma unroll
-    for (int rs = 0; rs < kRowSets; ++rs) {
-      float x[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[h * 4 + i] = sc[rs][h][i];
-      if (masked) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (st * kKeys + h * 16 + grp * 4 + i > row_pos[rs]) x[h * 4 + i] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      mx = reduce4rows<true>(mx) * a.scale_log2;
-      const bool move = mx > m_run[rs] + kSlack;
-      const float m_use = move ? mx : m_run[rs];
-      alpha[rs] = __builtin_amdgcn_exp2f(m_run[rs] - m_use);
-      moved |= move;
-      m_run[rs] = m_use;
-      float sum = 0.f;
-      __bf16 pe[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(x[e], a.scale_log2, -m_use));
-        sum += p;
-        pe[e] = static_cast<__bf16>(p);
-      }
-      l_run[rs] = l_run[rs] * alpha[rs] + sum;
-      pb[rs] = bf16x8{pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]};
-    }
-    if (__builtin_amdgcn_ballot_w64(moved)) {
-#pragma unroll
-      for (int rs = 0; rs < kRowSets; ++rs)
-#pragma unroll
-        for (int t = 0; t < kDimTiles; ++t) acc[rs][t] *= alpha[rs];
-    }
-
-    // ---- O^T += V^T P^T: A = V^T rows dim 16t+col, k index 8*grp+e = the
-    // keys of lane group grp in the interleaved V layout.
-#pragma unroll
-    for (int t = 0; t < kDimTiles; ++t) {
-      const bf16x8 va = *reinterpret_cast<const bf16x8*>(vl + (t * 16 + col) * 64 + grp * 16);
-#pragma unroll
-      for (int rs = 0; rs < kRowSets; ++rs)
-        acc[rs][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rs], acc[rs][t], 0, 0, 0);
-    }
-
-    if (more) store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[(st + 1) & 1]), plan, (st + 1) * kKeys, L, nxt);
+    if (st + 1 < nsteps)
+      store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[(st + 1) & 1]), plan, (st + 1) * kKeys, L, nxt);
     __syncthreads();
+  };
+  for (int st = 0; st < nsteps; st += 2) {
+    step(st, ra, rb);
+    if (st + 1 < nsteps) step(st + 1, rb, ra);
   }
 
-  // ---- normalise and store: lane holds dims 16t + 4*grp + i of row col.
+  // ---- normalise and store: lane holds dims 32t + 8(j/4) + 4*half + j%4 of its row.
+  const float l = reduce_pair<false>(l_run);
+  if (!row_ok) return;
+  const float inv = 1.f / l;
+  __bf16* orow = static_cast<__bf16*>(a.out) + row_q;
 #pragma unroll
-  for (int rs = 0; rs < kRowSets; ++rs) {
-    const float l = reduce4rows<false>(l_run[rs]);
-    if (!row_ok[rs]) continue;
-    const float inv = 1.f / l;
-    __bf16* orow = static_cast<__bf16*>(a.out) + row_q[rs];
+  for (int t = 0; t < kDimTiles; ++t)
 #pragma unroll
-    for (int t = 0; t < kDimTiles; ++t) {
-      const __bf16 o0 = static_cast<__bf16>(acc[rs][t][0] * inv), o1 = static_cast<__bf16>(acc[rs][t][1] * inv);
-      const __bf16 o2 = static_cast<__bf16>(acc[rs][t][2] * inv), o3 = static_cast<__bf16>(acc[rs][t][3] * inv);
-      uint2 w;
-      w.x = __builtin_bit_cast(uint16_t, o0) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o1)) << 16);
-      w.y = __builtin_bit_cast(uint16_t, o2) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o3)) << 16);
-      *reinterpret_cast<uint2*>(orow + t * 16 + grp * 4) = w;
+    for (int jq = 0; jq < 4; ++jq) {
+      uint32_t w[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const __bf16 o0 = static_cast<__bf16>(acc[t][4 * jq + 2 * e] * inv);
+        const __bf16 o1 = static_cast<__bf16>(acc[t][4 * jq + 2 * e + 1] * inv);
+        w[e] = __builtin_bit_cast(uint16_t, o0) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o1)) << 16);
+      }
+      *reinterpret_cast<uint2*>(orow + t * 32 + 8 * jq + 4 * half) = make_uint2(w[0], w[1]);
     }
-  }
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
