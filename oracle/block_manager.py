@@ -67,6 +67,26 @@ of different tenants apart.  Readings where they are silent:
   append without ids ends the sequence's chain (its later blocks are never
   registered).
 
+Swapping to host memory ("PagedAttention — Gestion mémoire pour LLM à long
+contexte", *Mode d'échec* and the glossary's *Page eviction*: when GPU
+memory runs out even with paging, cold pages are written to CPU RAM and
+read back when needed).  Readings where the pages are silent:
+
+* a host pool of fixed blocks in the pool's own format, with its own free
+  stack (element 0 handed out first, released blocks on top);
+* ``swap_out(sid)`` gives every block of the sequence, in logical order, a
+  fresh host block and reports the (GPU block, host block) copies; the
+  sequence then drops its GPU references exactly as ``free_seq`` would
+  (shared blocks stay for their other holders, registered ones become
+  evictable).  A swapped-out sequence cannot be appended to, forked or
+  exported; ``free_seq`` releases its host blocks;
+* ``swap_in(sid)`` gives every host block, in logical order, a fresh GPU
+  block (free stack first, then the eviction list), reports the (host
+  block, GPU block) copies and releases the host blocks; the new blocks are
+  unregistered (the sequence's digests are kept for later blocks);
+* both are atomic: with too few free blocks on the target side nothing
+  changes.
+
 Pins (``tests/test_oracle_block_manager.py``): after every operation the
 reference counts equal a from-scratch recount over all tables, free and
 used blocks partition the pool, every table has ``ceil(L/bs)`` entries;
@@ -146,6 +166,73 @@ class BlockManagerModel:
         self.cached = {}  # digest -> registered block
         self.block_digest = [None] * num_blocks
         self.lru = []  # evictable registered blocks, oldest first
+        # host swap pool
+        self.num_host_blocks = 0
+        self.host_free = []  # stack, top = end
+        self.host_tables = {}  # sid -> host blocks of a swapped-out sequence
+
+    def add_host_pool(self, num_host_blocks):
+        if self.num_host_blocks:
+            raise InvalidArg("the host pool is already set")
+        if num_host_blocks <= 0:
+            raise InvalidArg("num_host_blocks must be positive")
+        self.num_host_blocks = num_host_blocks
+        self.host_free = list(reversed(range(num_host_blocks)))
+
+    def _on_gpu(self, sid):
+        if sid not in self.tables:
+            raise UnknownSeq(f"unknown sequence {sid}")
+        if sid in self.host_tables:
+            raise InvalidArg(f"sequence {sid} is swapped out")
+
+    def _release(self, table):
+        for b in table:
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0 and self.block_digest[b] is None:
+                self.free.append(b)
+        for b in reversed(table):
+            if self.refcount[b] == 0 and self.block_digest[b] is not None:
+                self.lru.append(b)
+
+    def swap_out(self, sid):
+        """Move a sequence to the host pool; returns (GPU block, host block) copies."""
+        self._on_gpu(sid)
+        table = self.tables[sid]
+        if len(table) > len(self.host_free):
+            raise OutOfBlocks("not enough free host blocks")
+        pairs = []
+        for b in table:
+            h = self.host_free.pop()
+            pairs.append((b, h))
+        self.host_tables[sid] = [h for _, h in pairs]
+        self._release(table)
+        self.tables[sid] = []
+        return pairs
+
+    def swap_in(self, sid):
+        """Bring a swapped-out sequence back; returns (host block, GPU block) copies."""
+        if sid not in self.tables:
+            raise UnknownSeq(f"unknown sequence {sid}")
+        if sid not in self.host_tables:
+            raise InvalidArg(f"sequence {sid} is not swapped out")
+        hosts = self.host_tables[sid]
+        if len(hosts) > self._available():
+            raise OutOfBlocks("not enough free blocks")
+        pairs = []
+        table = []
+        for h in hosts:
+            b = self._take()
+            self.refcount[b] = 1
+            table.append(b)
+            pairs.append((h, b))
+        self.tables[sid] = table
+        for h in hosts:
+            self.host_free.append(h)
+        del self.host_tables[sid]
+        return pairs
+
+    def num_free_host(self):
+        return len(self.host_free)
 
     def _take(self):
         if self.free:
@@ -205,6 +292,7 @@ class BlockManagerModel:
     def fork(self, parent, child, n):
         if parent not in self.tables:
             raise UnknownSeq(f"unknown parent {parent}")
+        self._on_gpu(parent)
         if child in self.tables:
             raise InvalidArg(f"sequence {child} exists")
         if n < 0 or n > self.lens[parent]:
@@ -221,14 +309,10 @@ class BlockManagerModel:
     def free_seq(self, sid):
         if sid not in self.tables:
             raise UnknownSeq(f"unknown sequence {sid}")
-        table = self.tables[sid]
-        for b in table:
-            self.refcount[b] -= 1
-            if self.refcount[b] == 0 and self.block_digest[b] is None:
-                self.free.append(b)
-        for b in reversed(table):
-            if self.refcount[b] == 0 and self.block_digest[b] is not None:
-                self.lru.append(b)
+        if sid in self.host_tables:
+            self.host_free.extend(self.host_tables.pop(sid))
+        else:
+            self._release(self.tables[sid])
         for m in (self.tables, self.lens, self.salt, self.tokens, self.digests):
             del m[sid]
 
@@ -283,6 +367,7 @@ class BlockManagerModel:
         for sid, n in zip(sids, ntoks):
             if sid not in self.tables:
                 raise UnknownSeq(f"unknown sequence {sid}")
+            self._on_gpu(sid)
             if n < 0:
                 raise InvalidArg("negative token count")
         total = sum(ntoks)
@@ -344,8 +429,7 @@ class BlockManagerModel:
     def block_tables(self, sids, max_blocks):
         rows, lens = [], []
         for sid in sids:
-            if sid not in self.tables:
-                raise UnknownSeq(f"unknown sequence {sid}")
+            self._on_gpu(sid)
             t = self.tables[sid]
             if len(t) > max_blocks:
                 raise Capacity("table wider than max_blocks")
@@ -372,6 +456,9 @@ class BlockManagerModel:
         """Raise AssertionError if the bookkeeping is inconsistent."""
         recount = [0] * self.num_blocks
         for sid, t in self.tables.items():
+            if sid in self.host_tables:
+                assert t == [] and len(self.host_tables[sid]) == _cdiv(self.lens[sid], self.block_size)
+                continue
             assert len(t) == _cdiv(self.lens[sid], self.block_size), "table length != ceil(L/bs)"
             for b in t:
                 recount[b] += 1
@@ -383,6 +470,10 @@ class BlockManagerModel:
         assert len(lru) == len(self.lru), "block twice on the eviction list"
         assert not (free & used) and not (lru & used) and not (free & lru), "block in two of free/evictable/used"
         assert len(free) + len(lru) + len(used) == self.num_blocks, "block neither free, evictable nor in use"
+        host_used = [h for t in self.host_tables.values() for h in t]
+        assert len(set(host_used)) == len(host_used), "host block held twice"
+        assert not (set(host_used) & set(self.host_free)), "host block both free and held"
+        assert len(host_used) + len(self.host_free) == self.num_host_blocks, "host block lost"
         # digest registry: a bijection between digests and registered blocks
         assert len(self.cached) == sum(d is not None for d in self.block_digest)
         for d, b in self.cached.items():
@@ -395,6 +486,8 @@ class BlockManagerModel:
         # registered block it holds carries the digest of its position
         bs = self.block_size
         for sid, t in self.tables.items():
+            if sid in self.host_tables:
+                continue
             known, digests = self.tokens[sid], self.digests[sid]
             assert len(known) <= self.lens[sid] and len(digests) <= self.lens[sid] // bs
             d = ZERO_DIGEST

@@ -37,6 +37,7 @@ __all__ = [
     "copy_blocks",
     "gather",
     "to_f64",
+    "swap_copy",
 ]
 
 
@@ -93,6 +94,14 @@ def copy_blocks(k_pool, v_pool, pairs):
     for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
         k_pool[dst] = k_pool[src].copy()
         v_pool[dst] = v_pool[src].copy()
+
+
+def swap_copy(src_k, src_v, dst_k, dst_v, pairs):
+    """Whole-block copies between two pools of the same format (device pool
+    and host swap pool): ``dst[d] = src[s]`` for every ``(s, d)``."""
+    for s, d in pairs:
+        dst_k[d] = src_k[s]
+        dst_v[d] = src_v[s]
 
 
 def gather(k_pool, v_pool, table_row, length):
