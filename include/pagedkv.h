@@ -111,6 +111,18 @@ int32_t paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ds
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                              pkv_dtype dt, void* stream);
 
+/* Whole-block copies between two pools of the same format (the device    */
+/* pool and a host swap pool, either way): for each pair (s, d),          */
+/* dst[d] = src[s] for K and V, all kv heads ([sheet] Page eviction).     */
+/* Each of src_k, src_v, dst_k, dst_v may be device memory or pinned host */
+/* memory (read or written in place over the bus; pageable host memory is */
+/* rejected).  pairs: device (or pinned host) int32 [num_pairs][2]; pairs */
+/* naming blocks outside [0, src_num_blocks) or [0, dst_num_blocks) are  */
+/* skipped.  Asynchronous on `stream`.                                     */
+int32_t paged_kv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int32_t* pairs,
+                             int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t src_num_blocks, int32_t dst_num_blocks, pkv_dtype dt, void* stream);
+
 /* ------------------------------------------------------------------ */
 /* Decode attention ([pl] Jak działa and Komponenty: an attention kernel  */
 /* that reads a non-contiguous cache through the block table; [aitalk]   */
@@ -350,6 +362,42 @@ int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t
                           int32_t stage_capacity, int32_t* block_tables, int32_t max_blocks_per_seq,
                           int32_t* context_lens, int32_t* slot_mapping, int32_t* cow_pairs, int32_t cow_capacity,
                           int32_t full, int32_t* n_cow_out, int32_t* max_len_out, void* stream);
+
+/* ---- Swap to host memory -------------------------------------------- */
+/* [sheet] Mode d'échec and the glossary's Page eviction: when GPU memory */
+/* runs out even with paged allocation, pages are written to CPU RAM and  */
+/* read back when needed.  The host pool has the device pool's format and */
+/* its own block ids 0..num_host_blocks-1; the caller owns its memory     */
+/* (pinned, e.g. hipHostMalloc / pin_memory) and runs the copies with     */
+/* paged_kv_swap_blocks.                                                  */
+/* Policy: a host free stack (id 0 handed out first, released ids on top).*/
+
+/* Give the manager a host pool of num_host_blocks blocks (once).          */
+int32_t pkv_bm_add_host_pool(pkv_block_manager* bm, int32_t num_host_blocks);
+
+/* Move a sequence to the host pool: each of its blocks, in logical order, */
+/* gets a fresh host block; pairs_out [capacity][2] receives (GPU block,   */
+/* host block) copies to run before the GPU blocks are reused, and *n_pairs_out */
+/* their count.  The sequence then drops its GPU references as            */
+/* pkv_bm_free_seq would (blocks shared with other sequences stay, blocks */
+/* with a prefix-cache digest become evictable).  While swapped out it    */
+/* cannot be appended to, forked, exported or staged (PKV_ERR_INVALID_ARG);*/
+/* pkv_bm_free_seq releases its host blocks.  PKV_ERR_OUT_OF_BLOCKS if    */
+/* the host pool is short; atomic.                                        */
+int32_t pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs_out, int32_t capacity,
+                        int32_t* n_pairs_out);
+
+/* Bring a swapped-out sequence back: each host block, in logical order,  */
+/* gets a fresh GPU block (free stack first, then the oldest evictable    */
+/* block); pairs_out receives (host block, GPU block) copies to run       */
+/* before the sequence is used; the host blocks are released.  The new    */
+/* blocks carry no prefix-cache digest.  Atomic.                           */
+int32_t pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs_out, int32_t capacity,
+                       int32_t* n_pairs_out);
+
+int32_t pkv_bm_num_free_host(const pkv_block_manager* bm);
+/* 1 if the sequence is swapped out, 0 if not, negative on error.          */
+int32_t pkv_bm_is_swapped(const pkv_block_manager* bm, int64_t seq_id);
 
 /* Worst-case stage size (int32 count) for pkv_bm_stage_step.              */
 int32_t pkv_bm_stage_capacity(int32_t n_seqs, int32_t max_blocks_per_seq);

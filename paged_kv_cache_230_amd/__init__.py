@@ -9,6 +9,7 @@ from ._native import EXPORTED, LIB_PATH, PKVError, last_error  # noqa: F401
 from .api import (  # noqa: F401
     BlockManager,
     block_digest,
+    host_pools,
     new_pools,
     paged_attention_decode,
     paged_attention_prefill,
@@ -16,6 +17,7 @@ from .api import (  # noqa: F401
     paged_attention_workspace_bytes,
     paged_kv_append,
     paged_kv_copy_blocks,
+    paged_kv_swap_blocks,
     pool_shapes,
 )
 from .cache import PagedKVCache  # noqa: F401

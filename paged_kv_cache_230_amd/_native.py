@@ -89,6 +89,12 @@ _SIGS = {
         _i32, [_vp, _pi64, _i32, _pi32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _pi32, _pi32, _vp]),
     "pkv_bm_stage_capacity": (_i32, [_i32, _i32]),
     "pkv_block_digest": (_i32, [_pu8, _u64, _pi32, _i32, _pu8]),
+    "paged_kv_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_bm_add_host_pool": (_i32, [_vp, _i32]),
+    "pkv_bm_swap_out": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pkv_bm_swap_in": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pkv_bm_num_free_host": (_i32, [_vp]),
+    "pkv_bm_is_swapped": (_i32, [_vp, _i64]),
     "pkv_bm_add_seq_cached": (_i32, [_vp, _i64, _pi32, _i32, _u64, _pi32]),
     "pkv_bm_match_prefix": (_i32, [_vp, _pi32, _i32, _u64]),
     "pkv_bm_num_cached": (_i32, [_vp]),

@@ -70,6 +70,12 @@ def new_pools(num_blocks, num_kv_heads, head_dim, block_size, dtype, device="cud
     return torch.zeros(ks, dtype=dtype, device=device), torch.zeros(vs, dtype=dtype, device=device)
 
 
+def host_pools(num_blocks, num_kv_heads, head_dim, block_size, dtype):
+    """A host swap pool (K, V) in the device pool's format, in pinned memory."""
+    ks, vs = pool_shapes(num_blocks, num_kv_heads, head_dim, block_size, dtype)
+    return torch.zeros(ks, dtype=dtype, pin_memory=True), torch.zeros(vs, dtype=dtype, pin_memory=True)
+
+
 def _pool_dims(k_cache, v_cache):
     _need(k_cache, "k_cache", ndim=5)
     _need(v_cache, "v_cache", dtype=k_cache.dtype, device=k_cache.device, ndim=4)
@@ -164,6 +170,36 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         )
     )
     return out
+
+
+def paged_kv_swap_blocks(src_k, src_v, dst_k, dst_v, pairs):
+    """Whole-block copies ``dst[d] = src[s]`` between a device pool and a
+    host swap pool (either direction; host pools must be pinned).
+
+    ``pairs``: int32 ``[n][2]`` (source block, destination block), on the
+    device or in pinned host memory.  Runs on the current stream of the
+    device pool's GPU."""
+    dev = src_k.device if src_k.is_cuda else dst_k.device
+    nb_s, H, _, bs, _ = src_k.shape
+    nb_d = dst_k.shape[0]
+    d = src_v.shape[2]
+    for t, name in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    if src_k.shape[1:] != dst_k.shape[1:] or src_v.shape[1:] != dst_v.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination pools must have the same block format")
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
+        raise ValueError("pairs must be a contiguous int32 [n][2] tensor")
+    if not (pairs.is_cuda or pairs.is_pinned()):
+        raise ValueError("pairs must be on the GPU or in pinned host memory")
+    N.check(
+        N.lib.paged_kv_swap_blocks(
+            _ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(pairs), pairs.shape[0], H, d, bs, nb_s, nb_d,
+            _dt(src_k.dtype), _stream(dev),
+        )
+    )
 
 
 def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len,
@@ -283,6 +319,31 @@ class BlockManager:
         N.check(N.lib.pkv_bm_add_seq_cached(self._h, int(seq_id), _i32p(toks), toks.shape[0], _salt(salt),
                                             C.byref(n)))
         return n.value
+
+    def add_host_pool(self, num_host_blocks: int):
+        N.check(N.lib.pkv_bm_add_host_pool(self._h, int(num_host_blocks)))
+        self.num_host_blocks = int(num_host_blocks)
+
+    def _swap(self, fn, seq_id):
+        cap = max(self.num_blocks, getattr(self, "num_host_blocks", 0), 1)
+        pairs = np.empty((cap, 2), np.int32)
+        n = C.c_int32(0)
+        N.check(fn(self._h, int(seq_id), _i32p(pairs), cap, C.byref(n)))
+        return pairs[: n.value].copy()
+
+    def swap_out(self, seq_id: int):
+        """Move a sequence to the host pool; returns (GPU block, host block) pairs to copy."""
+        return self._swap(N.lib.pkv_bm_swap_out, seq_id)
+
+    def swap_in(self, seq_id: int):
+        """Bring a sequence back; returns (host block, GPU block) pairs to copy."""
+        return self._swap(N.lib.pkv_bm_swap_in, seq_id)
+
+    def num_free_host(self) -> int:
+        return N.check(N.lib.pkv_bm_num_free_host(self._h))
+
+    def is_swapped(self, seq_id: int) -> bool:
+        return bool(N.check(N.lib.pkv_bm_is_swapped(self._h, int(seq_id))))
 
     def match_prefix(self, tokens, salt: int = 0) -> int:
         toks = _ids32(tokens, len(tokens))

@@ -40,6 +40,14 @@
 //     fork inside it) copies it first even for its only holder; a block
 //     released that way joins the eviction list after the whole call, so no
 //     copy of the call reads a block the same call hands out again.
+//
+// Swapping to host memory ("PagedAttention — Gestion mémoire pour LLM à long
+// contexte", Mode d'échec and the glossary's Page eviction: when GPU memory
+// runs out even with paging, pages go to CPU RAM and come back on demand):
+// a host pool with its own free stack; swap-out gives each block of a
+// sequence, in logical order, a fresh host block and then drops the GPU
+// references as a free would; swap-in takes fresh GPU blocks (free stack,
+// then eviction list) and releases the host blocks.  Both are atomic.
 #include <algorithm>
 #include <cstdint>
 #include <new>
@@ -60,6 +68,9 @@ struct pkv_block_manager {
     uint64_t salt = 0;
     std::vector<int32_t> tokens;
     std::vector<pkv::Digest> digests;
+    // Swapped out: the table is empty and host_table holds the host blocks.
+    bool swapped = false;
+    std::vector<int32_t> host_table;
     // Device mirror (pkv_bm_stage_step): row of the device table this
     // sequence was last written to (-1: none), entries written there, and the
     // lowest entry changed since (a copy-on-write replacement).
@@ -80,6 +91,9 @@ struct pkv_block_manager {
   std::vector<uint8_t> registered;
   std::vector<int32_t> lru_prev, lru_next;
   int32_t lru_head = -1, lru_tail = -1, lru_size = 0;
+  // Host swap pool.
+  int32_t num_host_blocks = 0;
+  std::vector<int32_t> host_free;  // back() is handed out next
   // Device table the mirror state refers to, and the sequence whose entries
   // each of its rows last received.
   const void* mirror_table = nullptr;
@@ -150,6 +164,23 @@ void complete_block(BM* bm, BM::Seq& s, int32_t i) {
     bm->block_digest[b] = d;
     bm->registered[b] = 1;
   }
+}
+
+// Drops one reference from each block of a table: blocks reaching zero go
+// to the free stack in logical order, registered ones to the eviction list
+// from the last to the first.
+void release_table(BM* bm, const std::vector<int32_t>& t) {
+  for (int32_t b : t) {
+    if (--bm->refcount[b] == 0 && !bm->registered[b]) bm->free_stack.push_back(b);
+  }
+  for (auto r = t.rbegin(); r != t.rend(); ++r) {
+    if (bm->refcount[*r] == 0 && bm->registered[*r]) lru_push_back(bm, *r);
+  }
+}
+
+int32_t check_on_gpu(const BM::Seq& s, int64_t id) {
+  if (s.swapped) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %lld is swapped out", (long long)id);
+  return PKV_OK;
 }
 
 // Registered blocks for the leading full blocks of a prompt, up to the first miss.
@@ -260,6 +291,7 @@ int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child, int32_
   if (int32_t e = check_handle(bm)) return e;
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown parent sequence %lld", (long long)parent);
+  if (int32_t e = check_on_gpu(it->second, parent)) return e;
   if (bm->seqs.count(child)) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %lld already exists", (long long)child);
   if (num_tokens < 0 || num_tokens > it->second.len)
     return pkv::fail(PKV_ERR_INVALID_ARG, "fork length %d outside the parent's context [0, %d]", num_tokens,
@@ -297,6 +329,7 @@ int32_t pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32
   for (int32_t i = 0; i < n_seqs; ++i) {
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    if (int32_t e = check_on_gpu(it->second, seq_ids[i])) return e;
     if (!seen.insert(seq_ids[i]).second)
       return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %lld appears twice in one call", (long long)seq_ids[i]);
     const int32_t n = num_tokens ? num_tokens[i] : 1;
@@ -375,12 +408,10 @@ int32_t pkv_bm_free_seq(pkv_block_manager* bm, int64_t seq_id) {
   if (int32_t e = check_handle(bm)) return e;
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
-  const auto& t = it->second.table;
-  for (int32_t b : t) {
-    if (--bm->refcount[b] == 0 && !bm->registered[b]) bm->free_stack.push_back(b);
-  }
-  for (auto r = t.rbegin(); r != t.rend(); ++r) {
-    if (bm->refcount[*r] == 0 && bm->registered[*r]) lru_push_back(bm, *r);
+  if (it->second.swapped) {
+    for (int32_t h : it->second.host_table) bm->host_free.push_back(h);
+  } else {
+    release_table(bm, it->second.table);
   }
   bm->seqs.erase(it);
   return pkv::ok();
@@ -396,6 +427,7 @@ int32_t pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids,
   for (int32_t i = 0; i < n_seqs; ++i) {
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    if (int32_t e = check_on_gpu(it->second, seq_ids[i])) return e;
     if (static_cast<int64_t>(it->second.table.size()) > max_blocks_per_seq)
       return pkv::fail(PKV_ERR_CAPACITY, "sequence %lld holds %zu blocks > max_blocks_per_seq %d",
                        (long long)seq_ids[i], it->second.table.size(), max_blocks_per_seq);
@@ -470,6 +502,84 @@ int32_t pkv_bm_free_stack(const pkv_block_manager* bm, int32_t* out, int32_t cap
 }
 
 
+int32_t pkv_bm_add_host_pool(pkv_block_manager* bm, int32_t num_host_blocks) {
+  if (int32_t e = check_handle(bm)) return e;
+  if (bm->num_host_blocks) return pkv::fail(PKV_ERR_INVALID_ARG, "the host pool is already set");
+  if (num_host_blocks <= 0) return pkv::fail(PKV_ERR_INVALID_ARG, "num_host_blocks must be positive");
+  bm->num_host_blocks = num_host_blocks;
+  bm->host_free.resize(num_host_blocks);
+  for (int32_t i = 0; i < num_host_blocks; ++i) bm->host_free[num_host_blocks - 1 - i] = i;
+  return pkv::ok();
+}
+
+int32_t pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs_out, int32_t capacity,
+                        int32_t* n_pairs_out) {
+  if (int32_t e = check_handle(bm)) return e;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  auto& q = it->second;
+  if (int32_t e = check_on_gpu(q, seq_id)) return e;
+  const int32_t n = static_cast<int32_t>(q.table.size());
+  if (capacity < n) return pkv::fail(PKV_ERR_CAPACITY, "pair buffer holds %d pairs, %d needed", capacity, n);
+  if (n > 0 && !pairs_out) return pkv::fail(PKV_ERR_INVALID_ARG, "pairs_out is null");
+  if (static_cast<size_t>(n) > bm->host_free.size())
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "%d host blocks needed, %zu free", n, bm->host_free.size());
+  q.host_table.resize(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t h = bm->host_free.back();
+    bm->host_free.pop_back();
+    pairs_out[2 * i] = q.table[i];
+    pairs_out[2 * i + 1] = h;
+    q.host_table[i] = h;
+  }
+  release_table(bm, q.table);
+  q.table.clear();
+  q.swapped = true;
+  q.mirror_row = -1;  // its device-table row is rewritten in full after swap-in
+  if (n_pairs_out) *n_pairs_out = n;
+  return pkv::ok();
+}
+
+int32_t pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs_out, int32_t capacity,
+                       int32_t* n_pairs_out) {
+  if (int32_t e = check_handle(bm)) return e;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  auto& q = it->second;
+  if (!q.swapped) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %lld is not swapped out", (long long)seq_id);
+  const int32_t n = static_cast<int32_t>(q.host_table.size());
+  if (capacity < n) return pkv::fail(PKV_ERR_CAPACITY, "pair buffer holds %d pairs, %d needed", capacity, n);
+  if (n > 0 && !pairs_out) return pkv::fail(PKV_ERR_INVALID_ARG, "pairs_out is null");
+  if (n > available(bm))
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "%d blocks needed, %lld free", n, (long long)available(bm));
+  q.table.resize(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = take_block(bm);
+    bm->refcount[b] = 1;
+    q.table[i] = b;
+    pairs_out[2 * i] = q.host_table[i];
+    pairs_out[2 * i + 1] = b;
+  }
+  for (int32_t h : q.host_table) bm->host_free.push_back(h);
+  q.host_table.clear();
+  q.swapped = false;
+  q.mirror_row = -1;
+  if (n_pairs_out) *n_pairs_out = n;
+  return pkv::ok();
+}
+
+int32_t pkv_bm_num_free_host(const pkv_block_manager* bm) {
+  if (int32_t e = check_handle(bm)) return e;
+  return static_cast<int32_t>(bm->host_free.size());
+}
+
+int32_t pkv_bm_is_swapped(const pkv_block_manager* bm, int64_t seq_id) {
+  if (int32_t e = check_handle(bm)) return e;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  return it->second.swapped ? 1 : 0;
+}
+
 int32_t pkv_bm_stage_capacity(int32_t n_seqs, int32_t max_blocks_per_seq) {
   if (n_seqs < 0 || max_blocks_per_seq < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "negative size");
   const int64_t need = 4 + 4 * static_cast<int64_t>(n_seqs) + 3 * static_cast<int64_t>(n_seqs) * max_blocks_per_seq;
@@ -507,6 +617,7 @@ int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t
   for (int32_t i = 0; i < n_seqs; ++i) {
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    if (int32_t e = check_on_gpu(it->second, seq_ids[i])) return e;
     const auto& q = it->second;
     const bool owned = !remap && q.mirror_row == i && i < static_cast<int32_t>(bm->row_owner.size()) &&
                        bm->row_owner[i] == seq_ids[i];
