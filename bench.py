@@ -36,6 +36,8 @@ if ROOT not in sys.path:
 
 METRIC = "decode attention KV GB/s (% of HBM peak) and tokens/s, 70B-shaped layer @32k"
 PREFILL_METRIC = "chunked-prefill attention TFLOP/s (causal, 70B-shaped layer)"
+SWAP_METRIC = "swap to pinned host memory and back, GB/s per direction (70B-shaped 32k sequences)"
+HOST_LINK_PEAK = 64.0e9  # PCIe 5.0 x16, one direction, bytes/s
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 MFMA_BF16_PEAK = 2.5e15  # MI355X dense bf16 matrix-core flop/s
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_230_amd", "csrc", "pagedkv_kernels.hip")
@@ -327,6 +329,113 @@ def prefill_cpu_baseline(w, num_seqs):
     }
 
 
+# --------------------------------------------------------------- swap leg
+def run_swap(args, w, dev):
+    """Consecutive swap steps: all sequences out to the pinned host pool
+    (bookkeeping, pair upload, device -> host block copies), then back in
+    (host -> device).  Each direction is timed with HIP events around its
+    copy kernel; the block bookkeeping runs on the host beforehand."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_230_amd as pkv
+
+    c = w.config
+    nsteps = args.warmup + args.steps
+    cache = pkv.PagedKVCache(w.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.torch_dtype, dev,
+                             w.free_order)
+    for op in w.setup_ops:
+        cache.apply(op, w.kv)
+    bm = cache.bm
+    bm.add_host_pool(w.host_blocks)
+    hk, hv = pkv.host_pools(w.host_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.torch_dtype)
+    block_bytes = 2 * c.num_kv_heads * c.block_size * c.head_dim * c.elem_bytes
+    seqs = list(w.decode_seqs)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nsteps)]
+    moved = []
+    torch.cuda.synchronize()
+
+    def step(k):
+        out_pairs = np.concatenate([bm.swap_out(s) for s in seqs])
+        d_out = torch.from_numpy(out_pairs).to(dev)
+        in_pairs = np.concatenate([bm.swap_in(s) for s in seqs])
+        d_in = torch.from_numpy(in_pairs).to(dev)
+        ev[k][0].record()
+        pkv.paged_kv_swap_blocks(cache.k_cache, cache.v_cache, hk, hv, d_out)
+        ev[k][1].record()
+        pkv.paged_kv_swap_blocks(hk, hv, cache.k_cache, cache.v_cache, d_in)
+        ev[k][2].record()
+        moved.append((len(out_pairs) * block_bytes, len(in_pairs) * block_bytes))
+        torch.cuda.synchronize()  # the pair buffers are reused next step
+
+    for k in range(args.warmup):
+        step(k)
+    t0 = time.perf_counter()
+    for k in range(args.warmup, nsteps):
+        step(k)
+    elapsed = time.perf_counter() - t0
+    timed = range(args.warmup, nsteps)
+    out_s = [ev[k][0].elapsed_time(ev[k][1]) / 1e3 for k in timed]
+    in_s = [ev[k][1].elapsed_time(ev[k][2]) / 1e3 for k in timed]
+    out_b = sum(moved[k][0] for k in timed)
+    in_b = sum(moved[k][1] for k in timed)
+    d2h = out_b / sum(out_s)
+    h2d = in_b / sum(in_s)
+    slow = min(d2h, h2d)
+    return {
+        "metric": SWAP_METRIC,
+        "value": round((out_b + in_b) / (sum(out_s) + sum(in_s)) / 1e9, 2),  # one direction at a time
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": len(seqs), "context_len": int(w.lengths[0]) - 1,
+                   "bytes_each_way_per_step": moved[-1][0], "num_kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
+                   "block_size": c.block_size},
+        "swap_out_gbps": round(d2h / 1e9, 2),
+        "swap_in_gbps": round(h2d / 1e9, 2),
+        "swap_out_ms": round(1e3 * sum(out_s) / len(out_s), 3),
+        "swap_in_ms": round(1e3 * sum(in_s) / len(in_s), 3),
+        "roofline": {
+            "bound": "host_link",
+            "kernel": "paged_kv_swap_blocks (slower direction: " + ("device->host" if d2h <= h2d else "host->device") + ")",
+            "achieved": round(slow / 1e9, 2),
+            "peak": HOST_LINK_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": round(slow / HOST_LINK_PEAK, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+
+
+def swap_cpu_baseline(w):
+    """The oracle's block copy (oracle.pool.swap_copy) timed on the host for
+    one sequence's blocks, device-pool format to host-pool format."""
+    import numpy as np
+
+    import oracle.pool as opool
+
+    c = w.config
+    nblk = -(-(int(w.lengths[0]) - 1) // c.block_size)
+    src = opool.new_pools(nblk, c.num_kv_heads, c.head_dim, c.block_size, np.uint16, fill=1)
+    dst = opool.new_pools(nblk, c.num_kv_heads, c.head_dim, c.block_size, np.uint16)
+    pairs = [(b, nblk - 1 - b) for b in range(nblk)]
+    t0 = time.perf_counter()
+    opool.swap_copy(src[0], src[1], dst[0], dst[1], pairs)
+    dt = time.perf_counter() - t0
+    nbytes = nblk * 2 * c.num_kv_heads * c.block_size * c.head_dim * c.elem_bytes
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "seconds": dt, "cores": 1, "kind": "oracle",
+            "sample": f"oracle swap_copy of one 32k-token sequence ({nblk} blocks, {nbytes / 1e6:.0f} MB) "
+                      "between two NumPy pools"}
+
+
 # ----------------------------------------------------------------- GPU leg
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -358,6 +467,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = Workload(args.workload)
+    if hasattr(w, "host_blocks"):
+        result = run_swap(args, w, dev)
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = swap_cpu_baseline(w)
+        print(json.dumps(result), flush=True)
+        return
     if hasattr(w, "chunk_lens"):
         result = run_prefill(args, w, dev)
         if not args.no_cpu_baseline:

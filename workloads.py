@@ -38,6 +38,9 @@ The five workloads follow the configurations the task is measured on:
   step appends a chunk of uniform [128, 1024] new tokens per sequence (the
   same length each step) and runs causal attention of the chunk over the
   whole cache.  Block 16, 48k-block pool.
+* ``c8_swap_bf16`` -- swapping: 4 sequences of 32768 tokens of the
+  70B-shaped layer (block 16, 10k-block pool) and a host pool holding all
+  of them; a step swaps the 4 out to host memory and back in.
 
 Reading of the length convention: a stated context length is the number of
 tokens the decode attention reads *including* the token appended in that
@@ -104,6 +107,7 @@ CONFIGS = {
     "c5_mixed_bs32_bf16": Config("c5_mixed_bs32_bf16", "bf16", 64, 8, 128, 32, 128 ** -0.5, 235, steps=10),
     "c6_prefix_cache_bf16": Config("c6_prefix_cache_bf16", "bf16", 32, 8, 128, 16, 128 ** -0.5, 236),
     "c7_prefill_bf16": Config("c7_prefill_bf16", "bf16", 64, 8, 128, 16, 128 ** -0.5, 237),
+    "c8_swap_bf16": Config("c8_swap_bf16", "bf16", 64, 8, 128, 16, 128 ** -0.5, 238),
 }
 
 # Stress variants of the value distribution (same shapes).  With the
@@ -160,6 +164,7 @@ class Workload:
             "c5_mixed_bs32_bf16": self._build_plain_c5,
             "c6_prefix_cache_bf16": self._build_cached,
             "c7_prefill_bf16": self._build_prefill,
+            "c8_swap_bf16": self._build_swap,
         }[self.name]
         builder(rng)
 
@@ -266,6 +271,11 @@ class Workload:
         self.lengths = np.array([self.prefix_len + int(self.suffix_lens[r]) + 1 for r in self.decode_seqs],
                                 dtype=np.int64)
         self.tracks_tokens = True
+
+    def _build_swap(self, rng):
+        lengths = np.full(int(self.overrides.get("num_seqs", 4)), 32768)
+        self._finish_plain(rng, lengths, 10000)
+        self.host_blocks = int(self.overrides.get("host_blocks", len(lengths) * 2048 + 64))
 
     def _build_prefill(self, rng):
         """Histories in the cache, then chunks of new tokens every step."""
