@@ -411,6 +411,50 @@ int32_t pkv_bm_num_seqs(const pkv_block_manager* bm);
 /* capacity >= pkv_bm_num_free().                                          */
 int32_t pkv_bm_free_stack(const pkv_block_manager* bm, int32_t* out, int32_t capacity);
 
+/* ---- Radix-tree prefix index ---------------------------------------- */
+/* [aitalk] RadixAttention : un arbre qui n'oublie pas, and the paragraph */
+/* after it: a compressed trie over token sequences; a request walks it   */
+/* token by token for the longest cached prefix and reuses its K/V; paths */
+/* are inserted for later requests; least recently used leaves are        */
+/* evicted first, nodes that requests depend on are kept; the tree only   */
+/* points at blocks of the paged allocator.                               */
+/* Every node is backed by a block-manager sequence (its holder, ids       */
+/* 2^62 + k in creation order) forked from the request or from the node   */
+/* it splits, so the tree adds references, not blocks.  A match may end   */
+/* inside a block: the request then shares that partial block and the     */
+/* block manager copies it on the request's first write (copy-on-write).  */
+/* Host only; the block manager must outlive the index.                    */
+typedef struct pkv_radix pkv_radix;
+int32_t pkv_radix_create(pkv_block_manager* bm, pkv_radix** out);
+/* Frees the index and releases every holder sequence. */
+void pkv_radix_destroy(pkv_radix* rx);
+/* Longest cached prefix of tokens[0..n_tokens) in tokens (>= 0).          */
+int32_t pkv_radix_match(const pkv_radix* rx, const int32_t* tokens, int32_t n_tokens);
+/* Register request `seq_id` (a new block-manager sequence) for a prompt: */
+/* it shares the longest cached prefix (*n_cached_out tokens; it forks    */
+/* the deepest matched node's holder) or starts empty; the matched nodes  */
+/* are locked until pkv_radix_release and stamped with the current time.  */
+/* The caller appends tokens[*n_cached_out..].  Error if the id exists.   */
+int32_t pkv_radix_admit(pkv_radix* rx, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                        int32_t* n_cached_out);
+/* Make the first n_tokens tokens of sequence seq_id (its K/V written)     */
+/* reusable: an edge that diverges part way is split there, the rest      */
+/* becomes a new leaf; *n_added_out = tokens added to the tree.            */
+int32_t pkv_radix_insert(pkv_radix* rx, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                         int32_t* n_added_out);
+/* Unlock what pkv_radix_admit locked for seq_id (the sequence itself is  */
+/* freed with pkv_bm_free_seq).                                            */
+int32_t pkv_radix_release(pkv_radix* rx, int64_t seq_id);
+/* Free the holders of unlocked leaves, least recently used first (ties:  */
+/* the older node), until pkv_bm_num_free() >= num_free_blocks or nothing */
+/* is evictable; *n_evicted_out = nodes freed.                             */
+int32_t pkv_radix_evict(pkv_radix* rx, int32_t num_free_blocks, int32_t* n_evicted_out);
+int32_t pkv_radix_num_nodes(const pkv_radix* rx);
+/* Nodes depth-first, children by first token: holder id, depth, edge     */
+/* length, lock count and time stamp; returns the count.                   */
+int32_t pkv_radix_nodes(const pkv_radix* rx, int64_t* holders, int32_t* depths, int32_t* edge_lens, int32_t* locks,
+                        int64_t* stamps, int32_t capacity);
+
 #ifdef __cplusplus
 }
 #endif

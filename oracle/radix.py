@@ -141,6 +141,8 @@ class RadixCacheModel:
             raise UnknownSeq(f"unknown sequence {sid}")
         if len(tokens) > self.bm.lens[sid]:
             raise InvalidArg("more tokens than the sequence holds")
+        if sid in self.bm.host_tables:
+            raise InvalidArg(f"sequence {sid} is swapped out")
         path, m, used = self._walk(tokens)
         self.clock += 1
         for n in path:

@@ -8,6 +8,7 @@ Importing fails if the library has not been built (no CPU fallback).
 from ._native import EXPORTED, LIB_PATH, PKVError, last_error  # noqa: F401
 from .api import (  # noqa: F401
     BlockManager,
+    RadixIndex,
     block_digest,
     host_pools,
     new_pools,

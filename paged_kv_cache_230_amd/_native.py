@@ -95,6 +95,15 @@ _SIGS = {
     "pkv_bm_swap_in": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
     "pkv_bm_num_free_host": (_i32, [_vp]),
     "pkv_bm_is_swapped": (_i32, [_vp, _i64]),
+    "pkv_radix_create": (_i32, [_vp, C.POINTER(_vp)]),
+    "pkv_radix_destroy": (None, [_vp]),
+    "pkv_radix_match": (_i32, [_vp, _pi32, _i32]),
+    "pkv_radix_admit": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pkv_radix_insert": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pkv_radix_release": (_i32, [_vp, _i64]),
+    "pkv_radix_evict": (_i32, [_vp, _i32, _pi32]),
+    "pkv_radix_num_nodes": (_i32, [_vp]),
+    "pkv_radix_nodes": (_i32, [_vp, _pi64, _pi32, _pi32, _pi32, _pi64, _i32]),
     "pkv_bm_add_seq_cached": (_i32, [_vp, _i64, _pi32, _i32, _u64, _pi32]),
     "pkv_bm_match_prefix": (_i32, [_vp, _pi32, _i32, _u64]),
     "pkv_bm_num_cached": (_i32, [_vp]),

@@ -460,3 +460,56 @@ class BlockManager:
         buf = np.empty(max(self.num_free(), 1), np.int32)
         n = N.check(N.lib.pkv_bm_free_stack(self._h, _i32p(buf), buf.shape[0]))
         return buf[:n].tolist()
+
+
+class RadixIndex:
+    """Radix-tree prefix index over a BlockManager (pkv_radix_*): token-level
+    longest-prefix reuse, path insertion and LRU eviction of unlocked leaves."""
+
+    def __init__(self, bm: BlockManager):
+        h = C.c_void_p()
+        N.check(N.lib.pkv_radix_create(bm._h, C.byref(h)))
+        self._h = h
+        self.bm = bm  # the block manager must outlive the index
+        self._destroy = N.lib.pkv_radix_destroy
+
+    def close(self):
+        if getattr(self, "_h", None) and getattr(self.bm, "_h", None):
+            self._destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def match(self, tokens) -> int:
+        t = _ids32(tokens, len(tokens))
+        return N.check(N.lib.pkv_radix_match(self._h, _i32p(t), t.shape[0]))
+
+    def admit(self, seq_id: int, tokens) -> int:
+        """New request sharing the longest cached prefix; returns its length."""
+        t = _ids32(tokens, len(tokens))
+        n = C.c_int32(0)
+        N.check(N.lib.pkv_radix_admit(self._h, int(seq_id), _i32p(t), t.shape[0], C.byref(n)))
+        return n.value
+
+    def insert(self, seq_id: int, tokens) -> int:
+        t = _ids32(tokens, len(tokens))
+        n = C.c_int32(0)
+        N.check(N.lib.pkv_radix_insert(self._h, int(seq_id), _i32p(t), t.shape[0], C.byref(n)))
+        return n.value
+
+    def release(self, seq_id: int):
+        N.check(N.lib.pkv_radix_release(self._h, int(seq_id)))
+
+    def evict(self, num_free_blocks: int) -> int:
+        n = C.c_int32(0)
+        N.check(N.lib.pkv_radix_evict(self._h, int(num_free_blocks), C.byref(n)))
+        return n.value
+
+    def nodes(self):
+        """[(holder, depth, edge_len, locks, stamp)] depth-first, children by first token."""
+        cap = max(N.check(N.lib.pkv_radix_num_nodes(self._h)), 1)
+        h, st = np.empty(cap, np.int64), np.empty(cap, np.int64)
+        d, e, lk = (np.empty(cap, np.int32) for _ in range(3))
+        n = N.check(N.lib.pkv_radix_nodes(self._h, _i64p(h), _i32p(d), _i32p(e), _i32p(lk), _i64p(st), cap))
+        return list(zip(h[:n].tolist(), d[:n].tolist(), e[:n].tolist(), lk[:n].tolist(), st[:n].tolist()))

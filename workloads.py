@@ -41,6 +41,12 @@ The five workloads follow the configurations the task is measured on:
 * ``c8_swap_bf16`` -- swapping: 4 sequences of 32768 tokens of the
   70B-shaped layer (block 16, 10k-block pool) and a host pool holding all
   of them; a step swaps the 4 out to host memory and back in.
+* ``c9_multiturn_bf16`` -- multi-turn conversations: 8 conversations of 3
+  turns; a turn adds a user message of uniform [20, 400] tokens and a
+  response of uniform [10, 200] tokens (ids uniform in [0, 32000)), and a
+  turn's prompt is the whole conversation so far plus the new message.
+  K/V rows are a function of (conversation, position).  8B-shaped heads,
+  block 16, 4k-block pool.
 
 Reading of the length convention: a stated context length is the number of
 tokens the decode attention reads *including* the token appended in that
@@ -108,6 +114,7 @@ CONFIGS = {
     "c6_prefix_cache_bf16": Config("c6_prefix_cache_bf16", "bf16", 32, 8, 128, 16, 128 ** -0.5, 236),
     "c7_prefill_bf16": Config("c7_prefill_bf16", "bf16", 64, 8, 128, 16, 128 ** -0.5, 237),
     "c8_swap_bf16": Config("c8_swap_bf16", "bf16", 64, 8, 128, 16, 128 ** -0.5, 238),
+    "c9_multiturn_bf16": Config("c9_multiturn_bf16", "bf16", 32, 8, 128, 16, 128 ** -0.5, 239),
 }
 
 # Stress variants of the value distribution (same shapes).  With the
@@ -118,7 +125,8 @@ CONFIGS = {
 VARIANTS = ("plain", "q64", "q512", "needle", "large")
 
 _KEY_TAGS = {"prefill": 1, "step": 2, "q": 3, "prefix": 4, "suffix": 5, "needle": 6, "system": 7, "user": 8,
-             "system_tokens": 9, "user_tokens": 10, "step_tokens": 11, "chunk": 12, "chunk_q": 13}
+             "system_tokens": 9, "user_tokens": 10, "step_tokens": 11, "chunk": 12, "chunk_q": 13, "conv": 14,
+             "conv_tokens": 15, "turn_q": 16}
 VOCAB = 32000
 
 
@@ -165,6 +173,7 @@ class Workload:
             "c6_prefix_cache_bf16": self._build_cached,
             "c7_prefill_bf16": self._build_prefill,
             "c8_swap_bf16": self._build_swap,
+            "c9_multiturn_bf16": self._build_multiturn,
         }[self.name]
         builder(rng)
 
@@ -272,6 +281,42 @@ class Workload:
                                 dtype=np.int64)
         self.tracks_tokens = True
 
+    def _build_multiturn(self, rng):
+        """Turn t of conversation c: prompt = positions [0, prompt_end[c][t]),
+        then the response up to turn_end[c][t]."""
+        o = self.overrides
+        n_conv = int(o.get("num_convs", 8))
+        n_turns = int(o.get("num_turns", 3))
+        users = rng.integers(int(o.get("user_min", 20)), int(o.get("user_max", 400)) + 1, size=(n_conv, n_turns))
+        resps = rng.integers(int(o.get("resp_min", 10)), int(o.get("resp_max", 200)) + 1, size=(n_conv, n_turns))
+        self.num_blocks = int(o.get("num_blocks", 4000))
+        self.free_order = rng.permutation(self.num_blocks).astype(np.int32)
+        self.num_convs, self.num_turns = n_conv, n_turns
+        self.prompt_end, self.turn_end = [], []
+        for c in range(n_conv):
+            pe, te, end = [], [], 0
+            for t in range(n_turns):
+                end += int(users[c, t])
+                pe.append(end)
+                end += int(resps[c, t])
+                te.append(end)
+            self.prompt_end.append(pe)
+            self.turn_end.append(te)
+        self.conv_len = [te[-1] for te in self.turn_end]
+        self.setup_ops = []
+        self.decode_seqs = list(range(n_conv))
+        self.lengths = np.array(self.conv_len, dtype=np.int64)
+
+    def conv_tokens(self, c: int) -> np.ndarray:
+        """Token ids of conversation c, every position of every turn."""
+        return self._ints(("conv_tokens", c), self.conv_len[c])
+
+    def turn_q(self, t: int):
+        """Queries of the last token of turn t, one row per conversation."""
+        cfg = self.config
+        shape = (self.num_convs, cfg.num_q_heads, cfg.head_dim)
+        return self._randn(("turn_q", t), shape, cfg.value_std * self._q_scale()).to(cfg.torch_dtype)
+
     def _build_swap(self, rng):
         lengths = np.full(int(self.overrides.get("num_seqs", 4)), 32768)
         self._finish_plain(rng, lengths, 10000)
@@ -362,6 +407,8 @@ class Workload:
             return torch.cat([ks, ku]), torch.cat([vs, vu])
         elif key[0] == "chunk":
             T = int(sum(self.chunk_lens))
+        elif key[0] == "conv":
+            T = self.conv_len[int(key[1])]
         elif key[0] == "system":
             T = self.prefix_len
         elif key[0] == "user":
