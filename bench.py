@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "decode attention KV GB/s (% of HBM peak) and tokens/s, 70B-shaped layer @32k"
 PREFILL_METRIC = "chunked-prefill attention TFLOP/s (causal, 70B-shaped layer)"
 SWAP_METRIC = "swap to pinned host memory and back, GB/s per direction (70B-shaped 32k sequences)"
+MULTITURN_METRIC = "multi-turn prompt tokens reused from cache (radix index), fraction"
 HOST_LINK_PEAK = 64.0e9  # PCIe 5.0 x16, one direction, bytes/s
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 MFMA_BF16_PEAK = 2.5e15  # MI355X dense bf16 matrix-core flop/s
@@ -415,6 +416,126 @@ def run_swap(args, w, dev):
     }
 
 
+# ---------------------------------------------------------- multi-turn leg
+def multiturn_replay(w, kind):
+    """Host-only replay of the conversation stream through the radix index
+    (``kind == "radix"``) or chained block digests (``"hash"``): prompt
+    tokens reused, blocks in use at the end, host time per admission and
+    per insertion."""
+    import paged_kv_cache_230_amd as pkv
+
+    bs = w.config.block_size
+    bm = pkv.BlockManager(w.num_blocks, bs, w.free_order)
+    rx = pkv.RadixIndex(bm) if kind == "radix" else None
+    toks = [w.conv_tokens(i) for i in range(w.num_convs)]
+    reused = prompt = admits = inserts = 0
+    t_admit = t_insert = 0.0
+    for t in range(w.num_turns):
+        for i in range(w.num_convs):
+            sid = 100 * (t + 1) + i
+            pe, te = w.prompt_end[i][t], w.turn_end[i][t]
+            t0 = time.perf_counter()
+            m = rx.admit(sid, toks[i][:pe]) if rx else bm.add_seq_cached(sid, toks[i][:pe], 0)
+            t_admit += time.perf_counter() - t0
+            admits += 1
+            bm.append_slots([sid], [te - m], token_ids=toks[i][m:te])
+            if rx:
+                t0 = time.perf_counter()
+                rx.insert(sid, toks[i][:te])
+                t_insert += time.perf_counter() - t0
+                inserts += 1
+                rx.release(sid)
+            bm.free_seq(sid)
+            reused += m
+            prompt += pe
+    # blocks kept for reuse once every request has finished: held by radix
+    # holders, or carrying a digest on the eviction list
+    kept = w.num_blocks - bm.num_free() if rx else bm.num_cached()
+    if rx:
+        rx.close()
+    return {"reused_tokens": reused, "prompt_tokens": prompt, "fraction": round(reused / prompt, 4),
+            "blocks_kept_for_reuse": kept, "admit_us": round(1e6 * t_admit / admits, 2),
+            "insert_us": round(1e6 * t_insert / max(inserts, 1), 2)}
+
+
+def run_multiturn(args, w, dev):
+    """The conversation stream on the GPU through the radix index: per turn,
+    admissions, appends (copy-on-write of shared partial blocks), one decode
+    over all conversations (timed with HIP events), insertions."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_230_amd as pkv
+
+    c = w.config
+    radix = multiturn_replay(w, "radix")
+    hashed = multiturn_replay(w, "hash")
+    cache = pkv.PagedKVCache(w.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.torch_dtype, dev,
+                             w.free_order)
+    rx = pkv.RadixIndex(cache.bm)
+    kv = [tuple(x.to(dev) for x in w.kv(("conv", i))) for i in range(w.num_convs)]
+    toks = [w.conv_tokens(i) for i in range(w.num_convs)]
+    qs = [w.turn_q(t).to(dev) for t in range(w.num_turns)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.num_turns)]
+    kv_bytes = []
+    copies = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(w.num_turns):
+        sids = [100 * (t + 1) + i for i in range(w.num_convs)]
+        for i, sid in enumerate(sids):
+            pe, te = w.prompt_end[i][t], w.turn_end[i][t]
+            m = rx.admit(sid, toks[i][:pe])
+            _, pairs = cache.append([sid], [te - m], kv[i][0][m:te], kv[i][1][m:te])
+            copies += pairs.shape[0]
+        out = torch.empty_like(qs[t])
+        tables, lens, _, lh = cache.tables(sids)
+        ev[t][0].record()
+        pkv.paged_attention_decode(out, qs[t], cache.k_cache, cache.v_cache, tables, lens, int(lh.max()))
+        ev[t][1].record()
+        kv_bytes.append(decode_kv_bytes(lh, c.num_kv_heads, c.head_dim, c.elem_bytes))
+        for i, sid in enumerate(sids):
+            rx.insert(sid, toks[i][:w.turn_end[i][t]])
+            rx.release(sid)
+            cache.bm.free_seq(sid)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dec_s = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    rx.close()
+    return {
+        "metric": MULTITURN_METRIC,
+        "value": radix["fraction"],
+        "unit": "fraction of prompt tokens",
+        "n_gpus": 1,
+        "steps": w.num_turns,
+        "warmup": 0,
+        "ms_per_step": round(elapsed / w.num_turns * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_convs": w.num_convs, "num_turns": w.num_turns,
+                   "num_q_heads": c.num_q_heads, "num_kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
+                   "block_size": c.block_size},
+        "radix": radix,
+        "chained_digests": hashed,
+        "partial_blocks_copied_on_write": int(copies),
+        "decode_ms_per_turn": [round(1e3 * x, 4) for x in dec_s],
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attention_decode (one call per turn over all conversations)",
+            "achieved": round(sum(kv_bytes) / sum(dec_s) / 1e9, 2),
+            "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": round(sum(kv_bytes) / sum(dec_s) / HBM_PEAK, 4),
+            "traffic": None,
+            "note": "calls of a few MB are launch- and latency-bound; listed for completeness, not an HBM claim",
+        },
+        "cpu_baseline": None,
+    }
+
+
 def swap_cpu_baseline(w):
     """The oracle's block copy (oracle.pool.swap_copy) timed on the host for
     one sequence's blocks, device-pool format to host-pool format."""
@@ -467,6 +588,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = Workload(args.workload)
+    if hasattr(w, "num_convs"):
+        result = run_multiturn(args, w, dev)
+        print(json.dumps(result), flush=True)
+        return
     if hasattr(w, "host_blocks"):
         result = run_swap(args, w, dev)
         if not args.no_cpu_baseline:
