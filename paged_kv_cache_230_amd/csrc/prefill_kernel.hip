@@ -43,6 +43,9 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float float16v;
+// Plain vector types (not the HIP structs) so staged chunks stay in registers.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kPWaves = 4;
 constexpr int kPThreads = 64 * kPWaves;
@@ -68,8 +71,19 @@ struct PrefillArgs {
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t max_query_len;
+  int32_t num_seqs;
+  int32_t ntiles;  // query tiles of the longest chunk
   float scale_log2;
 };
+
+// Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its
+// own L2.  Workgroup b runs on XCD b % 8; the mapping below gives every
+// workgroup of one (sequence, kv head) pair the same XCD, so the pair's K/V
+// tiles, which all its query tiles stream in the same order, are fetched
+// into one L2 instead of eight.  Pairs are dealt to the XCDs round-robin
+// (pair i to XCD i % 8), and within an XCD a pair's tiles are dispatched
+// latest first (they read the most keys).
+constexpr int kXcds = 8;
 
 // One step's K and V in LDS.  K part: [kKeys/BS tiles][D/8][BS][8] bf16,
 // the pool's tile format (each 16-lane quarter of a QK A operand read is a
@@ -88,9 +102,12 @@ struct StageLayout {
   static_assert((2 * kBytes / 16) % kPThreads == 0, "stage must split evenly over the threads");
 };
 
+// Three stages: step st is consumed (PV) while step st + 1 is consumed
+// (QK) and step st + 2 is written.
+constexpr int kStages = 3;
 template <int D>
 struct PrefillSmem {
-  uint4 stage[2][StageLayout<D>::kStageBytes / 16];
+  u32x4 stage[kStages][StageLayout<D>::kStageBytes / 16];
   int32_t ids[kIdChunk];
 };
 
@@ -117,82 +134,93 @@ __device__ __forceinline__ float reduce_pair(float v) {
 }
 
 // Where each of a thread's 16-byte staging chunks comes from and goes to;
-// the same every step, only the block ids change.
+// the same every step, only the block ids change.  A wave's 64 chunks of one
+// load are a contiguous 1 KB run inside one (block, kv head) tile (tiles are
+// at least 2 KB and aligned to their size), so the tile a chunk belongs to is
+// the same across the wave: block ids and tile base addresses are uniform
+// (scalar registers) and each lane only adds a 32-bit offset.
 template <int D, int BS>
 struct StagePlan {
   static constexpr int kTileBytes = BS * D * 2;
-  const char* base[StageLayout<D>::kPerThread];  // pool + kv head tile + src (add id * stride)
-  int src[StageLayout<D>::kPerThread];   // byte offset inside the (block, kv head) tile
-  int tile[StageLayout<D>::kPerThread];  // tile of the step (0 .. kKeys/BS-1)
+  static_assert(kTileBytes >= 64 * 16 * 2, "a wave's chunk run must not straddle tiles");
+  const char* kbase;  // K pool + this kv head's tile (add id * stride)
+  const char* vbase;  // V pool + this kv head's tile
+  int tile[StageLayout<D>::kPerThread];  // tile of the step (0 .. kKeys/BS-1), wave-uniform
+  uint32_t src[StageLayout<D>::kPerThread];  // byte offset inside the (block, kv head) tile
   int dst[StageLayout<D>::kPerThread];   // K: byte offset in the K part; V: first key of the chunk in the step
   int dim[StageLayout<D>::kPerThread];   // V: the chunk's dim
   __device__ StagePlan(const PrefillArgs& a, int g) {
     // Chunk k of a thread lies in the K part exactly when k < kPerThread / 2
     // (the K part is the first half of the stage and threads stride it).
     constexpr int kHalf = StageLayout<D>::kPerThread / 2;
+    kbase = static_cast<const char*>(a.k_cache) + static_cast<int64_t>(g) * kTileBytes;
+    vbase = static_cast<const char*>(a.v_cache) + static_cast<int64_t>(g) * kTileBytes;
 #pragma unroll
     for (int k = 0; k < StageLayout<D>::kPerThread; ++k) {
       const int ov = (threadIdx.x + kPThreads * (k % kHalf)) * 16;
-      tile[k] = ov / kTileBytes;
-      src[k] = ov % kTileBytes;
-      dst[k] = k < kHalf ? ov : tile[k] * BS + (src[k] % (2 * BS)) / 2;  // V: first key of the chunk in the step
-      dim[k] = k < kHalf ? 0 : src[k] / (2 * BS);                        // V tile [D][BS]: 8 keys of one dim
-      base[k] = static_cast<const char*>(k < kHalf ? a.k_cache : a.v_cache) + g * kTileBytes + src[k];
+      tile[k] = __builtin_amdgcn_readfirstlane(ov / kTileBytes);
+      const int sv = ov % kTileBytes;
+      src[k] = static_cast<uint32_t>(sv);
+      dst[k] = k < kHalf ? ov : tile[k] * BS + (sv % (2 * BS)) / 2;  // V: first key of the chunk in the step
+      dim[k] = k < kHalf ? 0 : sv / (2 * BS);                        // V tile [D][BS]: 8 keys of one dim
     }
   }
 };
 
 // Staged block ids [chunk_base, chunk_base + kIdChunk) of the sequence,
-// clamped to the pool; -1 past the context.
+// clamped to the pool.  Past the context the id is 0: such a block is read
+// but never used (its keys are masked and its V slots zeroed in LDS).
 __device__ __forceinline__ void fill_ids(const PrefillArgs& a, const int32_t* table, int chunk_base, int nblk,
                                          int32_t* ids) {
   for (int i = threadIdx.x; i < kIdChunk; i += kPThreads) {
     const int lb = chunk_base + i;
-    ids[i] = lb < nblk ? clampi(table[lb], 0, a.num_blocks - 1) : -1;
+    ids[i] = lb < nblk ? clampi(table[lb], 0, a.num_blocks - 1) : 0;
   }
 }
 
 template <int D, int BS>
 __device__ __forceinline__ void load_stage(const StagePlan<D, BS>& pl, int64_t stride, const int32_t* ids,
-                                           int first, uint4 (&r)[StageLayout<D>::kPerThread]) {
+                                           int first, u32x4 (&r)[StageLayout<D>::kPerThread]) {
   constexpr int kTiles = kKeys / BS;
+  constexpr int kHalf = StageLayout<D>::kPerThread / 2;
   int32_t id[kTiles];
 #pragma unroll
-  for (int kt = 0; kt < kTiles; ++kt) id[kt] = ids[first + kt];  // uniform LDS reads
+  for (int kt = 0; kt < kTiles; ++kt) id[kt] = __builtin_amdgcn_readfirstlane(ids[first + kt]);
 #pragma unroll
   for (int k = 0; k < StageLayout<D>::kPerThread; ++k) {
     int b = id[0];
 #pragma unroll
-    for (int kt = 1; kt < kTiles; ++kt) b = pl.tile[k] == kt ? id[kt] : b;  // select: no dynamic indexing
-    r[k] = b >= 0 ? *reinterpret_cast<const uint4*>(pl.base[k] + b * stride) : make_uint4(0, 0, 0, 0);
+    for (int kt = 1; kt < kTiles; ++kt) b = pl.tile[k] == kt ? id[kt] : b;  // uniform select
+    const char* tb = (k < kHalf ? pl.kbase : pl.vbase) + static_cast<int64_t>(b) * stride;
+    r[k] = *reinterpret_cast<const u32x4*>(tb + pl.src[k]);
   }
 }
 
 template <int D, int BS>
 __device__ __forceinline__ void store_stage(char* dst, const StagePlan<D, BS>& pl, int key_base, int L,
-                                            uint4 (&r)[StageLayout<D>::kPerThread]) {
+                                            u32x4 (&r)[StageLayout<D>::kPerThread]) {
   constexpr int kHalf = StageLayout<D>::kPerThread / 2;
 #pragma unroll
-  for (int k = 0; k < kHalf; ++k) *reinterpret_cast<uint4*>(dst + pl.dst[k]) = r[k];
+  for (int k = 0; k < kHalf; ++k) *reinterpret_cast<u32x4*>(dst + pl.dst[k]) = r[k];
   char* vdst = dst + StageLayout<D>::kBytes;
   const bool tail = key_base + kKeys > L;  // uniform: only the step holding the context's end
 #pragma unroll
   for (int k = kHalf; k < StageLayout<D>::kPerThread; ++k) {
-    uint4 x = r[k];
+    u32x4 x = r[k];
     const int kk0 = pl.dst[k];  // first key of the chunk within the step (a multiple of 8)
     if (tail) {  // zero V slots at or past the context end
-      uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      uint32_t w[4] = {x[0], x[1], x[2], x[3]};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (key_base + kk0 + e >= L) w[e / 2] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-      x = make_uint4(w[0], w[1], w[2], w[3]);
+      x = u32x4{w[0], w[1], w[2], w[3]};
     }
     // keys kk0..kk0+3 go to group 2m, kk0+4..kk0+7 to group 2m+1, each at
     // element (kk0 % 16) / 8 * 4 of its group (m = kk0 / 16).
     const int m = kk0 / 16;
     char* row = vdst + pl.dim[k] * kVRow + ((kk0 % 16) / 8) * 8;
-    *reinterpret_cast<uint2*>(row + (2 * m) * 16) = make_uint2(x.x, x.y);
-    *reinterpret_cast<uint2*>(row + (2 * m + 1) * 16) = make_uint2(x.z, x.w);
+    *reinterpret_cast<u32x2*>(row + (2 * m) * 16) = u32x2{x[0], x[1]};
+    *reinterpret_cast<u32x2*>(row + (2 * m + 1) * 16) = u32x2{x[2], x[3]};
   }
 }
 
@@ -204,8 +232,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   // more than this (log2 units), so probabilities stay below 2^8 and the
   // accumulators are rescaled only on such moves.
   constexpr float kSlack = 8.f;
-  const int s = blockIdx.z;
-  const int g = blockIdx.y;
+  const int xcd = static_cast<int>(blockIdx.x) % kXcds, slot = static_cast<int>(blockIdx.x) / kXcds;
+  const int pair = xcd + kXcds * (slot / a.ntiles);
+  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int s = pair / a.num_kv_heads;
+  const int g = pair - s * a.num_kv_heads;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
@@ -217,7 +248,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   if (q0 + C > a.num_tokens) C = a.num_tokens - q0;
   const int TQ = a.tokens_per_tile;
   const int ntiles = (C + TQ - 1) / TQ;
-  const int tile = static_cast<int>(gridDim.x) - 1 - static_cast<int>(blockIdx.x);  // latest tiles first
+  const int tile = a.ntiles - 1 - slot % a.ntiles;  // latest tiles first
   if (tile >= ntiles) return;
   const int tok0 = tile * TQ;
   const int ntok = C - tok0 < TQ ? C - tok0 : TQ;
@@ -262,66 +293,82 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   for (int t = 0; t < kDimTiles; ++t) acc[t] = float16v{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Two register sets carry K/V two steps ahead: step j's chunks live in
-  // set j % 2 from the load issued during step j - 2 until they are written
-  // to LDS at the end of step j - 1.
-  uint4 ra[StageLayout<D>::kPerThread], rb[StageLayout<D>::kPerThread];
+  // Pipeline: during step st the PV product reads LDS stage st % 3, the QK
+  // product of step st + 1 reads stage (st + 1) % 3 (its MFMAs overlap this
+  // step's exponentials), and step st + 2's K/V, loaded into registers
+  // during step st - 1, are written to stage (st + 2) % 3 at the end.  Two
+  // register sets alternate: step st loads step st + 3 into one while the
+  // other holds step st + 2.
+  using Regs = u32x4[StageLayout<D>::kPerThread];
+  Regs r0, r1;
   int chunk_base = 0;
   fill_ids(a, table, 0, nblk, sm.ids);
   __syncthreads();
-  load_stage<D, BS>(plan, stride, sm.ids, 0, ra);
-  if (nsteps > 1) load_stage<D, BS>(plan, stride, sm.ids, kTiles, rb);
-  store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[0]), plan, 0, L, ra);
+  load_stage<D, BS>(plan, stride, sm.ids, 0, r0);
+  store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[0]), plan, 0, L, r0);
+  if (nsteps > 1) {
+    load_stage<D, BS>(plan, stride, sm.ids, kTiles, r1);
+    store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[1]), plan, kKeys, L, r1);
+  }
+  if (nsteps > 2) load_stage<D, BS>(plan, stride, sm.ids, 2 * kTiles, r0);
   __syncthreads();
 
   const int key_col = lane & 31;  // key of the QK A operand within the step
   const int k_tile = key_col / BS, k_in = key_col % BS;
-  auto step = [&](int st, uint4 (&cur)[StageLayout<D>::kPerThread], uint4 (&nxt)[StageLayout<D>::kPerThread]) {
-    // cur: free (step st is in LDS) -> receives step st + 2; nxt: holds step st + 1.
-    if (st + 2 < nsteps) {
-      if ((st + 2) * kTiles >= chunk_base + kIdChunk) {
+  const int k_off = k_tile * kTileBytes + (half * BS + k_in) * 16;
+  auto qk = [&](const char* kl) {
+    float16v r = float16v{};
+#pragma unroll
+    for (int c = 0; c < kQChunks; ++c) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + k_off + c * 2 * BS * 16);
+      r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[c], r, 0, 0, 0);
+    }
+    return r;
+  };
+  auto next = [](int c) { return c == kStages - 1 ? 0 : c + 1; };
+
+  auto step = [&](int st, int cur, Regs& ld, Regs& sv, const float16v& sc, float16v& sn)
+                  __attribute__((always_inline)) {
+    const int nx1 = next(cur), nx2 = next(nx1);
+    if (st + 3 < nsteps) {
+      if ((st + 3) * kTiles >= chunk_base + kIdChunk) {
         // Every read of the staged ids so far happened before the last barrier.
         chunk_base += kIdChunk;
         fill_ids(a, table, chunk_base, nblk, sm.ids);
         __syncthreads();
       }
-      load_stage<D, BS>(plan, stride, sm.ids, (st + 2) * kTiles - chunk_base, cur);
-    }
-    const char* kl = reinterpret_cast<const char*>(sm.stage[st & 1]);
-    const char* vl = kl + StageLayout<D>::kBytes;
-
-    // ---- S^T = K Q^T over the step's 32 keys.
-    float16v sc = float16v{};
-#pragma unroll
-    for (int c = 0; c < kQChunks; ++c) {
-      const bf16x8 ka =
-          *reinterpret_cast<const bf16x8*>(kl + k_tile * kTileBytes + ((c * 2 + half) * BS + k_in) * 16);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[c], sc, 0, 0, 0);
+      load_stage<D, BS>(plan, stride, sm.ids, (st + 3) * kTiles - chunk_base, ld);
     }
 
-    // ---- online softmax of this lane's 16 scores (keys 8(j/4)+4*half+j%4).
-    float x[16];  // scores in log2 units
+    // ---- row max of step st (raw scores; the scale is positive, so it
+    // commutes with the max and is folded into the exponent below).
+    float x[16];  // raw scores of keys 8(j/4)+4*half+j%4
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = sc[j] * a.scale_log2;
+    for (int j = 0; j < 16; ++j) x[j] = sc[j];
     if (st >= mask_from) {
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (st * kKeys + 8 * (j / 4) + 4 * half + (j % 4) > row_pos) x[j] = -INFINITY;
     }
-    float mx = x[0];
+    float mx = fmaxf(x[0], x[1]);
 #pragma unroll
-    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, x[j]);
-    mx = reduce_pair<true>(mx);
+    for (int j = 2; j < 16; ++j) mx = fmaxf(mx, x[j]);
+    mx = reduce_pair<true>(mx) * a.scale_log2;
     const bool move = mx > m_run + kSlack;
     const float m_use = move ? mx : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_use;
-    float sum = 0.f;
+
+    // ---- scores of step st + 1 (on the last step this reads a stage whose
+    // contents are unused: in bounds, result dropped).
+    sn = qk(reinterpret_cast<const char*>(sm.stage[nx1]));
+
     __bf16 pe[16];
+    float sum;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float p = __builtin_amdgcn_exp2f(x[j] - m_use);
-      sum += p;
+      const float p = __builtin_amdgcn_exp2f(fmaf(x[j], a.scale_log2, -m_use));
+      sum = j ? sum + p : p;
       pe[j] = static_cast<__bf16>(p);
     }
     l_run = l_run * alpha + sum;
@@ -333,6 +380,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     // ---- O^T += V^T P^T, two products of 16 keys: product m takes this
     // lane's scores j = 8m..8m+7, i.e. keys 16m+8(i/4)+4*half+i%4, which is
     // how group 2m+half of the V part orders them.
+    const char* vl = reinterpret_cast<const char*>(sm.stage[cur]) + StageLayout<D>::kBytes;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const bf16x8 pb = bf16x8{pe[8 * m], pe[8 * m + 1], pe[8 * m + 2], pe[8 * m + 3],
@@ -344,14 +392,20 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    if (st + 1 < nsteps)
-      store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[(st + 1) & 1]), plan, (st + 1) * kKeys, L, nxt);
+    if (st + 2 < nsteps)
+      store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[nx2]), plan, (st + 2) * kKeys, L, sv);
     __syncthreads();
   };
-  for (int st = 0; st < nsteps; st += 2) {
-    step(st, ra, rb);
-    if (st + 1 < nsteps) step(st + 1, rb, ra);
+
+  float16v s0 = qk(reinterpret_cast<const char*>(sm.stage[0])), s1;
+  int st = 0, cur = 0;
+  for (; st + 1 < nsteps; st += 2) {  // unrolled by two: register sets and score sets swap roles
+    step(st, cur, r1, r0, s0, s1);
+    cur = next(cur);
+    step(st + 1, cur, r0, r1, s1, s0);
+    cur = next(cur);
   }
+  if (st < nsteps) step(st, cur, r1, r0, s0, s1);
 
   // ---- normalise and store: lane holds dims 32t + 8(j/4) + 4*half + j%4 of its row.
   const float l = reduce_pair<false>(l_run);
@@ -408,8 +462,6 @@ int32_t paged_attention_prefill(void* out, const void* q, const void* k_cache, c
                      num_kv_heads);
   const int32_t G = num_q_heads / num_kv_heads;
   if (G > kRows) return pkv::fail(PKV_ERR_UNSUPPORTED, "query group size %d > %d not supported", G, kRows);
-  if (num_seqs > 65535 || num_kv_heads > 65535)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "num_seqs and num_kv_heads must be <= 65535");
   if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX ||
       static_cast<int64_t>(num_seqs) * max_blocks_per_seq > INT32_MAX)
     return pkv::fail(PKV_ERR_INVALID_ARG, "table size exceeds the int32 range");
@@ -421,7 +473,15 @@ int32_t paged_attention_prefill(void* out, const void* q, const void* k_cache, c
     return pkv::fail(PKV_ERR_INVALID_ARG, "q, out and the pools must be 16-byte aligned");
   const int32_t tq = kRows / G;
   const int64_t ntiles = (static_cast<int64_t>(max_query_len) + tq - 1) / tq;
-  if (ntiles > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "max_query_len too large");
+  // One workgroup per (pair, tile), pairs padded to a multiple of the XCD
+  // count; a launch holds at most 2^32 - 1 work-items.
+  const int64_t padded = (static_cast<int64_t>(num_seqs) * num_kv_heads + kXcds - 1) / kXcds * kXcds;
+  const int64_t max_blocks = UINT32_MAX / kPThreads;
+  if (padded > max_blocks || ntiles > max_blocks / padded)
+    return pkv::fail(PKV_ERR_INVALID_ARG,
+                     "launch too large: %lld (sequence, kv head) pairs x %lld query tiles exceeds %lld workgroups",
+                     static_cast<long long>(padded), static_cast<long long>(ntiles), static_cast<long long>(max_blocks));
+  const int64_t nblocks = padded * ntiles;
   PrefillArgs a;
   a.out = out;
   a.q = q;
@@ -438,8 +498,10 @@ int32_t paged_attention_prefill(void* out, const void* q, const void* k_cache, c
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_query_len = max_query_len;
+  a.num_seqs = num_seqs;
+  a.ntiles = static_cast<int32_t>(ntiles);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid(static_cast<uint32_t>(ntiles), static_cast<uint32_t>(num_kv_heads), static_cast<uint32_t>(num_seqs));
+  const dim3 grid(static_cast<uint32_t>(nblocks));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (head_dim == 128)
     dispatch_prefill_bs<128>(a, block_size, grid, st);
