@@ -210,9 +210,9 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
 /* max_query_len : host bound on the chunk lengths (sizes the launch)     */
 /* block_tables, context_lens, pools: as for paged_attention_decode       */
 /* scale         : > 0 (usually 1/sqrt(head_dim))                         */
-/* Query group sizes up to 128 are supported.  One launch holds at most  */
-/* 2^24 - 1 workgroups: num_seqs * num_kv_heads (rounded up to a multiple */
-/* of 8) times ceil(max_query_len * G / 128) query tiles; larger calls    */
+/* Query group sizes up to 256 are supported.  One launch holds at most  */
+/* 2^23 - 1 workgroups: num_seqs * num_kv_heads (rounded up to a multiple */
+/* of 8) times ceil(max_query_len * G / 256) query tiles; larger calls    */
 /* return PKV_ERR_INVALID_ARG.  No workspace; the kernel                  */
 /* clamps lengths, offsets and block ids to the given sizes, so bad       */
 /* device values give wrong rows, never accesses outside the buffers.    */

@@ -10,24 +10,24 @@
 // step 2), and paging leaves the result unchanged (its closing paragraph).
 //
 // Kernel design (gfx950, wave64, bf16 matrix cores):
-//   * One workgroup = 4 waves = one (query tile, kv head, sequence).  The
-//     128 score rows of a tile are (query token, query head) pairs of the
-//     G heads sharing the kv head, so every K/V byte staged serves G heads.
-//     Wave w owns rows 32w..32w+31, one per lane pair (l, l+32).
+//   * One workgroup = 8 waves = one (query tile, kv head, sequence), one
+//     workgroup per CU.  The 256 score rows of a tile are (query token,
+//     query head) pairs of the G heads sharing the kv head, so every K/V
+//     byte staged serves G heads.  Wave w owns rows 32w..32w+31, one per
+//     lane pair (l, l+32).  All tiles of one (sequence, kv head) pair run on
+//     one XCD, so they share its L2.
 //   * Keys advance 32 per step.  The step's K and V block tiles are copied
-//     into LDS in the pool's own format (double-buffered: the next step's
-//     global loads are in flight during this step's matrix work); block ids
-//     come from uniform (scalar) loads.  V slots past the context are
-//     zeroed in LDS, so unused slots of the last block never reach the
-//     products.
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the step's 32 keys in the
-//     rows, the wave's 32 query rows in the columns.  Lane l holds 16
-//     scores of row l%32 (keys 8(j/4)+4(l/32)+j%4), so a row's max needs one
-//     partner lane.  Those scores, in that order, are the B operand of the
-//     PV product once A (V^T, read from LDS) orders its k index the same
-//     way: O^T += V^T P^T, again 32x32x16.
-//   * Online softmax per row in the log2 domain; row maxima by gfx950 row
-//     swaps (v_permlane16/32_swap), not LDS shuffles; the causal mask (a
+//     into an 8-stage LDS ring by direct global-to-LDS loads issued 7 steps
+//     ahead, as permutations of the pool's 16-byte chunks (layouts at
+//     StageLayout); V slots past the context are zeroed in LDS, so unused
+//     slots of the last block never reach the products.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the step's 32 keys (in slot
+//     order) in the rows, the wave's 32 query rows in the columns.  Lane l
+//     holds 16 scores of row l%32, keys 16(j/8)+8(l/32)+j%8, so a row's max
+//     needs one partner lane, and those scores in that order are the B
+//     operand of the PV product: O^T += V^T P^T, again 32x32x16.
+//   * Online softmax per row in the log2 domain; row maxima by the gfx950
+//     row swap v_permlane32_swap, not LDS shuffles; the causal mask (a
 //     select, never a multiply) only on the steps that reach past the tile's
 //     first position.  A row's reference max moves only when its max grows
 //     by more than 2^8, so the accumulators are rescaled rarely; the
@@ -47,12 +47,11 @@ typedef __attribute__((ext_vector_type(16))) float float16v;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int kPWaves = 4;
+constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kRows = kPWaves * 32;  // score rows per workgroup (32 per wave)
 constexpr int kKeys = 32;                     // keys per step
-// Block ids of the tile's key range are staged in LDS this many at a time
-// (a vector load of a table entry per step would stall its wave).
+// Block ids of the tile's key range are staged in LDS this many at a time.
 constexpr int kIdChunk = 1024;
 
 struct PrefillArgs {
@@ -85,31 +84,67 @@ struct PrefillArgs {
 // latest first (they read the most keys).
 constexpr int kXcds = 8;
 
-// One step's K and V in LDS.  K part: [kKeys/BS tiles][D/8][BS][8] bf16,
-// the pool's tile format (each 16-lane quarter of a QK A operand read is a
-// contiguous 256-byte run).  V part: [D][4 groups][8] bf16, group 2m+h
-// holding keys 16m+4h+{0..3} then 16m+8+4h+{0..3}: the k order of PV
-// product m for lanes with l/32 = h, so each A operand is one 16-byte read;
-// rows are padded from 64 to 80 bytes so the 16 dims a quarter-wave reads
-// fall in distinct banks.
-constexpr int kVRow = 80;  // bytes per dim row of the V part
+// One step's K and V in LDS, each a copy of the step's kKeys/BS pool tiles
+// whose 16-byte chunks (8 bf16) are permuted, never split, so the copy is
+// done by direct global-to-LDS loads (global_load_lds_dwordx4: each lane
+// names its source chunk, the wave's 64 chunks land contiguously).
+//   K part: [kKeys/BS tiles][D/8][BS slots][8]; slot s holds key pi(s),
+//     pi swapping bits 2 and 3 of s.  Lane l of a QK A operand reads slot
+//     l % 32, so the product's output rows come out in key order pi, which
+//     makes a lane's 16 scores the keys 16(j/8) + 8(l/32) + j%8: per 16-key
+//     half, 8 consecutive keys, exactly the B operand of the PV product.
+//     Each 16-lane quarter of an A read is a contiguous 256-byte run.
+//   V part: [kKeys/BS tiles][D][BS/8 chunks][8], the pool's [D][BS] tile
+//     with the chunks of row d XOR-swizzled by vswz(d) so the 16 dims a
+//     quarter-wave reads hit distinct banks.
 template <int D>
 struct StageLayout {
-  static constexpr int kBytes = kKeys * D * 2;  // data bytes of the K or the V part
-  static constexpr int kVBytes = D * kVRow;     // V part with padding
-  static constexpr int kStageBytes = kBytes + kVBytes;
-  static constexpr int kPerThread = 2 * kBytes / 16 / kPThreads;  // 16-byte chunks per thread
-  static_assert((2 * kBytes / 16) % kPThreads == 0, "stage must split evenly over the threads");
+  static constexpr int kBytes = kKeys * D * 2;  // bytes of the K or the V part
+  static constexpr int kStageBytes = 2 * kBytes;
+  static constexpr int kPerThread = kStageBytes / 16 / kPThreads;  // DMA loads per thread per stage
+  static_assert((kStageBytes / 16) % kPThreads == 0, "stage must split evenly over the threads");
 };
 
-// Three stages: step st is consumed (PV) while step st + 1 is consumed
-// (QK) and step st + 2 is written.
-constexpr int kStages = 3;
+// Stage ring: during step st the PV product reads stage st, the QK product
+// of step st + 1 reads stage st + 1, and the loads of step st + kAhead are
+// issued into the stage step st - 1 used (all modulo kStages); the stages in
+// between are landing.
+constexpr int kStages = 8;
+constexpr int kAhead = kStages - 1;
 template <int D>
 struct PrefillSmem {
   u32x4 stage[kStages][StageLayout<D>::kStageBytes / 16];
   int32_t ids[kIdChunk];
 };
+
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+__device__ __forceinline__ int pi_slot(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
+
+template <int BS>
+__device__ __forceinline__ int vswz(int d) {
+  constexpr int n = BS / 8;  // chunks per V row
+  return (d * n / 8) % n;
+}
+
+// s_waitcnt with vmcnt(n), lgkmcnt(0) and no wait on export counts.
+template <int kN>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(kN >= 0 && kN < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(kN | (0x7 << 4));
+}
+
+// Workgroup barrier after this wave's LDS accesses and all but its newest kN
+// global-to-LDS loads have completed.  No memory fence (a fence would also
+// wait for the loads still in flight for later stages); the empty asm
+// statements keep the compiler from moving memory accesses across it.
+template <int kN>
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  wait_vm_lgkm0<kN>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
@@ -133,36 +168,60 @@ __device__ __forceinline__ float reduce_pair(float v) {
   return kMax ? fmaxf(b0, b1) : b0 + b1;
 }
 
-// Where each of a thread's 16-byte staging chunks comes from and goes to;
-// the same every step, only the block ids change.  A wave's 64 chunks of one
-// load are a contiguous 1 KB run inside one (block, kv head) tile (tiles are
-// at least 2 KB and aligned to their size), so the tile a chunk belongs to is
-// the same across the wave: block ids and tile base addresses are uniform
-// (scalar registers) and each lane only adds a 32-bit offset.
+// Barrier once all but the loads of this wave's newest n steps have landed
+// (n uniform, 0 <= n <= kN; the wait count must be an immediate).
+template <int kPer, int kN>
+__device__ __forceinline__ void barrier_after_steps(int n) {
+  if constexpr (kN == 0) {
+    stage_barrier<0>();
+  } else {
+    if (n >= kN)
+      stage_barrier<kN * kPer>();
+    else
+      barrier_after_steps<kPer, kN - 1>(n);
+  }
+}
+
+// Where each of a thread's DMA loads comes from and goes to; the same every
+// step, only the block ids change.  Load k of thread t fills LDS chunk
+// k * kPThreads + t of the stage, so a wave's load is a contiguous 1 KB run
+// inside one (block, kv head) tile (tiles are at least 2 KB and aligned to
+// their size): block ids, tile bases and LDS addresses are wave-uniform and
+// each lane adds a 32-bit source offset.
 template <int D, int BS>
 struct StagePlan {
   static constexpr int kTileBytes = BS * D * 2;
-  static_assert(kTileBytes >= 64 * 16 * 2, "a wave's chunk run must not straddle tiles");
+  static constexpr int kTileChunks = kTileBytes / 16;
+  static constexpr int kPartChunks = StageLayout<D>::kBytes / 16;  // chunks of the K (or V) part
+  static_assert(kTileChunks % 64 == 0 && kPartChunks % 64 == 0, "a wave's chunk run must not straddle tiles");
   const char* kbase;  // K pool + this kv head's tile (add id * stride)
   const char* vbase;  // V pool + this kv head's tile
-  int tile[StageLayout<D>::kPerThread];  // tile of the step (0 .. kKeys/BS-1), wave-uniform
+  int tile[StageLayout<D>::kPerThread];      // tile of the step (0 .. kKeys/BS-1), wave-uniform
+  bool vpart[StageLayout<D>::kPerThread];    // the load fills the V part, wave-uniform
   uint32_t src[StageLayout<D>::kPerThread];  // byte offset inside the (block, kv head) tile
-  int dst[StageLayout<D>::kPerThread];   // K: byte offset in the K part; V: first key of the chunk in the step
-  int dim[StageLayout<D>::kPerThread];   // V: the chunk's dim
+  int lds[StageLayout<D>::kPerThread];       // byte offset of the wave's run in the stage, wave-uniform
   __device__ StagePlan(const PrefillArgs& a, int g) {
-    // Chunk k of a thread lies in the K part exactly when k < kPerThread / 2
-    // (the K part is the first half of the stage and threads stride it).
-    constexpr int kHalf = StageLayout<D>::kPerThread / 2;
     kbase = static_cast<const char*>(a.k_cache) + static_cast<int64_t>(g) * kTileBytes;
     vbase = static_cast<const char*>(a.v_cache) + static_cast<int64_t>(g) * kTileBytes;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 #pragma unroll
     for (int k = 0; k < StageLayout<D>::kPerThread; ++k) {
-      const int ov = (threadIdx.x + kPThreads * (k % kHalf)) * 16;
-      tile[k] = __builtin_amdgcn_readfirstlane(ov / kTileBytes);
-      const int sv = ov % kTileBytes;
-      src[k] = static_cast<uint32_t>(sv);
-      dst[k] = k < kHalf ? ov : tile[k] * BS + (sv % (2 * BS)) / 2;  // V: first key of the chunk in the step
-      dim[k] = k < kHalf ? 0 : sv / (2 * BS);                        // V tile [D][BS]: 8 keys of one dim
+      const int p = k * kPThreads + static_cast<int>(threadIdx.x);  // chunk of the stage
+      const bool is_v = p >= kPartChunks;
+      const int pp = is_v ? p - kPartChunks : p;
+      vpart[k] = __builtin_amdgcn_readfirstlane(static_cast<int>(is_v)) != 0;
+      tile[k] = __builtin_amdgcn_readfirstlane(pp / kTileChunks);
+      const int r = pp % kTileChunks;
+      int chunk;
+      if (!is_v) {  // K: r = (d/8) * BS + slot
+        chunk = (r / BS) * BS + pi_slot(r % BS);
+      } else {      // V: r = d * (BS/8) + swizzled chunk
+        constexpr int n = BS / 8;
+        const int d = r / n;
+        chunk = d * n + ((r % n) ^ vswz<BS>(d));
+      }
+      src[k] = static_cast<uint32_t>(chunk) * 16u;
+      lds[k] = (k * kPThreads + wave * 64) * 16;
     }
   }
 };
@@ -178,54 +237,55 @@ __device__ __forceinline__ void fill_ids(const PrefillArgs& a, const int32_t* ta
   }
 }
 
+// One step's block ids as read from LDS (the same in every lane).  They are
+// read a step before their loads are issued and made scalar only then, so
+// the LDS read completes behind other work instead of stalling the wave.
+template <int BS>
+struct StepIds {
+  int32_t v[kKeys / BS];
+  __device__ __forceinline__ void read(const int32_t* ids, int first) {
+#pragma unroll
+    for (int kt = 0; kt < kKeys / BS; ++kt) v[kt] = ids[first + kt];
+  }
+};
+
+// Issue the DMA loads of one step into a stage.
 template <int D, int BS>
-__device__ __forceinline__ void load_stage(const StagePlan<D, BS>& pl, int64_t stride, const int32_t* ids,
-                                           int first, u32x4 (&r)[StageLayout<D>::kPerThread]) {
+__device__ __forceinline__ void load_stage(u32x4* stage, const StagePlan<D, BS>& pl, int64_t stride,
+                                           const StepIds<BS>& ids) {
   constexpr int kTiles = kKeys / BS;
-  constexpr int kHalf = StageLayout<D>::kPerThread / 2;
   int32_t id[kTiles];
 #pragma unroll
-  for (int kt = 0; kt < kTiles; ++kt) id[kt] = __builtin_amdgcn_readfirstlane(ids[first + kt]);
+  for (int kt = 0; kt < kTiles; ++kt) id[kt] = __builtin_amdgcn_readfirstlane(ids.v[kt]);
 #pragma unroll
   for (int k = 0; k < StageLayout<D>::kPerThread; ++k) {
     int b = id[0];
 #pragma unroll
     for (int kt = 1; kt < kTiles; ++kt) b = pl.tile[k] == kt ? id[kt] : b;  // uniform select
-    const char* tb = (k < kHalf ? pl.kbase : pl.vbase) + static_cast<int64_t>(b) * stride;
-    r[k] = *reinterpret_cast<const u32x4*>(tb + pl.src[k]);
+    const char* tb = (pl.vpart[k] ? pl.vbase : pl.kbase) + static_cast<int64_t>(b) * stride;
+    __builtin_amdgcn_global_load_lds(tb + pl.src[k], (LdsPtr)(reinterpret_cast<char*>(stage) + pl.lds[k]), 16, 0, 0);
   }
 }
 
+// Zero the V entries of keys at or past the context end L in a landed stage
+// (the stage holding the context's end; its unused slots may hold anything,
+// and a zero probability times a NaN would still be NaN).
 template <int D, int BS>
-__device__ __forceinline__ void store_stage(char* dst, const StagePlan<D, BS>& pl, int key_base, int L,
-                                            u32x4 (&r)[StageLayout<D>::kPerThread]) {
-  constexpr int kHalf = StageLayout<D>::kPerThread / 2;
-#pragma unroll
-  for (int k = 0; k < kHalf; ++k) *reinterpret_cast<u32x4*>(dst + pl.dst[k]) = r[k];
-  char* vdst = dst + StageLayout<D>::kBytes;
-  const bool tail = key_base + kKeys > L;  // uniform: only the step holding the context's end
-#pragma unroll
-  for (int k = kHalf; k < StageLayout<D>::kPerThread; ++k) {
-    u32x4 x = r[k];
-    const int kk0 = pl.dst[k];  // first key of the chunk within the step (a multiple of 8)
-    if (tail) {  // zero V slots at or past the context end
-      uint32_t w[4] = {x[0], x[1], x[2], x[3]};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (key_base + kk0 + e >= L) w[e / 2] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-      x = u32x4{w[0], w[1], w[2], w[3]};
+__device__ void zero_v_tail(u32x4* stage, int key_base, int L) {
+  constexpr int kTileBytes = BS * D * 2;
+  constexpr int n = BS / 8;
+  char* v = reinterpret_cast<char*>(stage) + StageLayout<D>::kBytes;
+  for (int i = threadIdx.x; i < D * kKeys; i += kPThreads) {
+    const int d = i / kKeys, key = i % kKeys;
+    if (key_base + key >= L) {
+      const int chunk = d * n + (((key % BS) / 8) ^ vswz<BS>(d));
+      *reinterpret_cast<uint16_t*>(v + (key / BS) * kTileBytes + chunk * 16 + (key % 8) * 2) = 0;
     }
-    // keys kk0..kk0+3 go to group 2m, kk0+4..kk0+7 to group 2m+1, each at
-    // element (kk0 % 16) / 8 * 4 of its group (m = kk0 / 16).
-    const int m = kk0 / 16;
-    char* row = vdst + pl.dim[k] * kVRow + ((kk0 % 16) / 8) * 8;
-    *reinterpret_cast<u32x2*>(row + (2 * m) * 16) = u32x2{x[0], x[1]};
-    *reinterpret_cast<u32x2*>(row + (2 * m + 1) * 16) = u32x2{x[2], x[3]};
   }
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillSmem<D> sm;
   constexpr int kTileBytes = BS * D * 2;
   // The reference max of a row moves only when the row max exceeds it by
@@ -293,27 +353,32 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   for (int t = 0; t < kDimTiles; ++t) acc[t] = float16v{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Pipeline: during step st the PV product reads LDS stage st % 3, the QK
-  // product of step st + 1 reads stage (st + 1) % 3 (its MFMAs overlap this
-  // step's exponentials), and step st + 2's K/V, loaded into registers
-  // during step st - 1, are written to stage (st + 2) % 3 at the end.  Two
-  // register sets alternate: step st loads step st + 3 into one while the
-  // other holds step st + 2.
-  using Regs = u32x4[StageLayout<D>::kPerThread];
-  Regs r0, r1;
+  // Pipeline (see kStages): the loads of step st + kAhead are issued at the
+  // top of step st; the barrier closing step st waits for this wave's loads
+  // of step st + 2 (all later steps' may still be in flight) and so
+  // publishes stage st + 2 before step st + 1 reads its K.
+  constexpr int kPer = StageLayout<D>::kPerThread;
   int chunk_base = 0;
   fill_ids(a, table, 0, nblk, sm.ids);
   __syncthreads();
-  load_stage<D, BS>(plan, stride, sm.ids, 0, r0);
-  store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[0]), plan, 0, L, r0);
-  if (nsteps > 1) {
-    load_stage<D, BS>(plan, stride, sm.ids, kTiles, r1);
-    store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[1]), plan, kKeys, L, r1);
+  StepIds<BS> ids;  // ids of the step whose loads are issued next
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    if (k < nsteps) {
+      ids.read(sm.ids, k * kTiles);
+      load_stage<D, BS>(sm.stage[k], plan, stride, ids);
+    }
   }
-  if (nsteps > 2) load_stage<D, BS>(plan, stride, sm.ids, 2 * kTiles, r0);
-  __syncthreads();
+  if (kAhead < nsteps) ids.read(sm.ids, kAhead * kTiles);
+  const bool tail = nsteps * kKeys > L;  // the last step reaches past the context end
+  // stages 0 and 1 landed; steps 2 .. min(kAhead, nsteps) - 1 may be in flight
+  barrier_after_steps<kPer, kAhead - 2>((nsteps < kAhead ? nsteps : kAhead) - 2);
+  if (nsteps == 1 && tail) {
+    zero_v_tail<D, BS>(sm.stage[0], 0, L);
+    stage_barrier<0>();
+  }
 
-  const int key_col = lane & 31;  // key of the QK A operand within the step
+  const int key_col = lane & 31;  // QK A operand slot of this lane
   const int k_tile = key_col / BS, k_in = key_col % BS;
   const int k_off = k_tile * kTileBytes + (half * BS + k_in) * 16;
   auto qk = [&](const char* kl) {
@@ -325,30 +390,42 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
     return r;
   };
-  auto next = [](int c) { return c == kStages - 1 ? 0 : c + 1; };
+  // V operand offsets: PV product m, dim tile t; lane dim 32t + l%32 reads
+  // keys 16m + 8(l/32) .. +7, i.e. chunk (16m + 8 half) / 8 of its row.
+  int v_off[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int key = 16 * m + 8 * half;
+    v_off[m] = StageLayout<D>::kBytes + (key / BS) * kTileBytes +
+               (key_col * (BS / 8) + (((key % BS) / 8) ^ vswz<BS>(key_col))) * 16;
+  }
+  static_assert(32 % (8 / (BS / 8)) == 0, "the V swizzle repeats within 32 dims");
 
-  auto step = [&](int st, int cur, Regs& ld, Regs& sv, const float16v& sc, float16v& sn)
-                  __attribute__((always_inline)) {
-    const int nx1 = next(cur), nx2 = next(nx1);
-    if (st + 3 < nsteps) {
-      if ((st + 3) * kTiles >= chunk_base + kIdChunk) {
-        // Every read of the staged ids so far happened before the last barrier.
-        chunk_base += kIdChunk;
-        fill_ids(a, table, chunk_base, nblk, sm.ids);
-        __syncthreads();
+  auto step = [&](int st, int cur, const float16v& sc, float16v& sn) __attribute__((always_inline)) {
+    const int nx1 = (cur + 1) % kStages, nxa = (cur + kAhead) % kStages;
+    if (st + kAhead < nsteps) {
+      load_stage<D, BS>(sm.stage[nxa], plan, stride, ids);
+      if (st + kAhead + 1 < nsteps) {
+        if ((st + kAhead + 1) * kTiles >= chunk_base + kIdChunk) {
+          // Every read of the staged ids so far happened before the last barrier.
+          chunk_base += kIdChunk;
+          fill_ids(a, table, chunk_base, nblk, sm.ids);
+          __syncthreads();
+        }
+        ids.read(sm.ids, (st + kAhead + 1) * kTiles - chunk_base);  // its loads are issued a step later
       }
-      load_stage<D, BS>(plan, stride, sm.ids, (st + 3) * kTiles - chunk_base, ld);
     }
+    if (tail && st + 1 == nsteps - 1) zero_v_tail<D, BS>(sm.stage[nx1], (st + 1) * kKeys, L);
 
     // ---- row max of step st (raw scores; the scale is positive, so it
     // commutes with the max and is folded into the exponent below).
-    float x[16];  // raw scores of keys 8(j/4)+4*half+j%4
+    float x[16];  // raw scores of keys 16(j/8) + 8*half + j%8
 #pragma unroll
     for (int j = 0; j < 16; ++j) x[j] = sc[j];
     if (st >= mask_from) {
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (st * kKeys + 8 * (j / 4) + 4 * half + (j % 4) > row_pos) x[j] = -INFINITY;
+        if (st * kKeys + 16 * (j / 8) + 8 * half + (j % 8) > row_pos) x[j] = -INFINITY;
     }
     float mx = fmaxf(x[0], x[1]);
 #pragma unroll
@@ -358,6 +435,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     const float m_use = move ? mx : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_use;
+    if (__builtin_amdgcn_ballot_w64(move)) {  // rare: before the products so they share one basic block
+#pragma unroll
+      for (int t = 0; t < kDimTiles; ++t) acc[t] *= alpha;
+    }
 
     // ---- scores of step st + 1 (on the last step this reads a stage whose
     // contents are unused: in bounds, result dropped).
@@ -372,40 +453,35 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
       pe[j] = static_cast<__bf16>(p);
     }
     l_run = l_run * alpha + sum;
-    if (__builtin_amdgcn_ballot_w64(move)) {
-#pragma unroll
-      for (int t = 0; t < kDimTiles; ++t) acc[t] *= alpha;
-    }
 
     // ---- O^T += V^T P^T, two products of 16 keys: product m takes this
-    // lane's scores j = 8m..8m+7, i.e. keys 16m+8(i/4)+4*half+i%4, which is
-    // how group 2m+half of the V part orders them.
-    const char* vl = reinterpret_cast<const char*>(sm.stage[cur]) + StageLayout<D>::kBytes;
+    // lane's scores j = 8m..8m+7, keys 16m + 8*half + i, the B operand's k
+    // order; the V operand of lane l holds the same keys of dim 32t + l%32.
+    const char* sl = reinterpret_cast<const char*>(sm.stage[cur]);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const bf16x8 pb = bf16x8{pe[8 * m], pe[8 * m + 1], pe[8 * m + 2], pe[8 * m + 3],
                                pe[8 * m + 4], pe[8 * m + 5], pe[8 * m + 6], pe[8 * m + 7]};
 #pragma unroll
       for (int t = 0; t < kDimTiles; ++t) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vl + (t * 32 + key_col) * kVRow + (2 * m + half) * 16);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(sl + v_off[m] + t * 32 * (BS / 8) * 16);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[t], 0, 0, 0);
       }
     }
 
-    if (st + 2 < nsteps)
-      store_stage<D, BS>(reinterpret_cast<char*>(sm.stage[nx2]), plan, (st + 2) * kKeys, L, sv);
-    __syncthreads();
+    // stage st + 2 landed; steps st + 3 .. min(st + kAhead, nsteps - 1) may be in flight
+    barrier_after_steps<kPer, kAhead - 2>((nsteps - 1 - st < kAhead ? nsteps - 1 - st : kAhead) - 2);
   };
 
   float16v s0 = qk(reinterpret_cast<const char*>(sm.stage[0])), s1;
   int st = 0, cur = 0;
-  for (; st + 1 < nsteps; st += 2) {  // unrolled by two: register sets and score sets swap roles
-    step(st, cur, r1, r0, s0, s1);
-    cur = next(cur);
-    step(st + 1, cur, r0, r1, s1, s0);
-    cur = next(cur);
+  for (; st + 1 < nsteps; st += 2) {  // unrolled by two: the score sets swap roles
+    step(st, cur, s0, s1);
+    cur = (cur + 1) % kStages;
+    step(st + 1, cur, s1, s0);
+    cur = (cur + 1) % kStages;
   }
-  if (st < nsteps) step(st, cur, r1, r0, s0, s1);
+  if (st < nsteps) step(st, cur, s0, s1);
 
   // ---- normalise and store: lane holds dims 32t + 8(j/4) + 4*half + j%4 of its row.
   const float l = reduce_pair<false>(l_run);

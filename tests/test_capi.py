@@ -82,13 +82,14 @@ def test_prefill_host_validation():
     assert call(d=96) == N.PKV_ERR_UNSUPPORTED
     assert call(bs=8) == N.PKV_ERR_UNSUPPORTED
     assert call(Hq=9) == N.PKV_ERR_INVALID_ARG
-    assert call(Hq=258) == N.PKV_ERR_UNSUPPORTED  # G = 129 > 128
+    assert call(Hq=514) == N.PKV_ERR_UNSUPPORTED  # G = 257 > 256
     assert call(scale=0.0) == N.PKV_ERR_INVALID_ARG
     assert call(S=0) == 0 and call(mq=0) == 0
-    # launch limit: (pairs rounded up to 8) * query tiles <= (2^32 - 1) / 256 workgroups
+    # launch limit: (pairs rounded up to 8) * query tiles <= (2^32 - 1) / 512 workgroups
     assert call(S=65536, Hkv=256, Hq=256, mq=1) == N.PKV_ERR_INVALID_ARG  # 2^24 pairs
     assert "launch too large" in N.last_error()
-    assert call(S=2 ** 20, Hkv=8, Hq=64, mq=32) == N.PKV_ERR_INVALID_ARG  # 2^23 pairs x 2 tiles
+    assert call(S=2 ** 20, Hkv=8, Hq=64, mq=32) == N.PKV_ERR_INVALID_ARG  # 2^23 pairs x 1 tile
+    assert "launch too large" in N.last_error()
     assert call(S=2 ** 31 - 1, Hkv=2 ** 31 - 1, Hq=2 ** 31 - 1, mb=1, mq=2 ** 31 - 1) == N.PKV_ERR_INVALID_ARG
     assert "launch too large" in N.last_error()  # no 64-bit overflow in the size check
 

@@ -37,7 +37,8 @@ SHAPES = [  # (q heads, kv heads, head_dim, block size)
     (8, 8, 128, 32),    # G 1
     (40, 8, 64, 16),    # G 5: a tile of 25 tokens, 3 idle rows
     (64, 8, 64, 32),    # G 8, head_dim 64, block 32
-    (128, 1, 128, 16),  # G 128: one token per tile
+    (128, 1, 128, 16),  # G 128: two tokens per tile
+    (256, 1, 64, 32),   # G 256: one token per tile
 ]
 
 
