@@ -607,7 +607,11 @@ def main():
         return
     c = w.config
     S = w.num_seqs
-    nsteps = args.warmup + args.steps
+    # Warm-up steps, the timed steps (no markers between kernels: each event
+    # marker costs a dispatch gap), then a pass of marked steps whose HIP
+    # events time each decode call for the roofline figure.
+    n_marked = min(args.steps, 10)
+    nsteps = args.warmup + args.steps + n_marked
     print(f"# setup {w.name}: {S} sequences, pool {w.num_blocks} blocks", file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
     cache = pkv.PagedKVCache(w.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.torch_dtype, dev,
@@ -640,15 +644,13 @@ def main():
     lens_d = torch.empty(S, dtype=torch.int32, device=dev)
     slots_d = torch.empty(S, dtype=torch.int32, device=dev)
     pairs_d = torch.empty(S, 2, dtype=torch.int32, device=dev)
-    # Two pinned step records, alternated.  A record is rewritten only after
-    # the GPU has read it: the decode-end event of the step that used it
-    # (recorded after that step's staging kernel) has completed.  No extra
-    # event is recorded for this, since every marker costs a dispatch gap.
-    RING = 2
+    # One pinned step record per step, so the host never waits for the GPU to
+    # release one (and no event is needed for that).
     stage_cap = pkv.BlockManager.stage_capacity(S, max_blocks)
-    stage = [torch.zeros(stage_cap, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
+    stage = [torch.zeros(stage_cap, dtype=torch.int32, pin_memory=True) for _ in range(nsteps)]
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
     ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
+    marked = range(args.warmup + args.steps, nsteps)
     host_s = [0.0] * nsteps
     seg = {"wait": 0.0, "bookkeeping+stage": 0.0, "copy+append": 0.0, "decode": 0.0}
     step_lens = []
@@ -657,25 +659,24 @@ def main():
     def step(k):
         nonlocal n_cow_total
         th = time.perf_counter()
-        r = k % RING
-        if k >= RING:
-            ev1[k - RING].synchronize()  # the GPU has read record r
         t1 = time.perf_counter()
-        n_cow, max_len = bm.stage_step(seqs, stage[r], tables_d, lens_d, slots_d, pairs_d, token_ids=step_ids[k])
-        step_lens.append(stage[r].numpy()[4 + S: 4 + 2 * S].copy())  # lengths in the record
+        n_cow, max_len = bm.stage_step(seqs, stage[k], tables_d, lens_d, slots_d, pairs_d, token_ids=step_ids[k])
+        step_lens.append(stage[k].numpy()[4 + S: 4 + 2 * S].copy())  # lengths in the record
         t2 = time.perf_counter()
         if n_cow:
             pkv.paged_kv_copy_blocks(cache.k_cache, cache.v_cache, pairs_d[:n_cow])
             n_cow_total += n_cow
         pkv.paged_kv_append(step_k[k], step_v[k], cache.k_cache, cache.v_cache, slots_d)
         t3 = time.perf_counter()
-        ev0[k].record()
+        if k in marked:
+            ev0[k].record()
         pkv.paged_attention_decode(out, step_q[k], cache.k_cache, cache.v_cache, tables_d, lens_d, max_len,
                                    partition_size=P, workspace=workspace)
-        ev1[k].record()
+        if k in marked:
+            ev1[k].record()
         t4 = time.perf_counter()
         host_s[k] = t4 - th
-        if k >= args.warmup:
+        if args.warmup <= k < args.warmup + args.steps:
             for name, dt in (("wait", t1 - th), ("bookkeeping+stage", t2 - t1), ("copy+append", t3 - t2),
                              ("decode", t4 - t3)):
                 seg[name] += dt
@@ -692,10 +693,13 @@ def main():
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for k in range(args.warmup, nsteps):
+    for k in range(args.warmup, args.warmup + args.steps):
         step(k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    for k in marked:
+        step(k)
+    torch.cuda.synchronize()
     print(f"# timed {args.steps} steps in {elapsed:.4f}s; host us/step by segment: "
           + ", ".join(f"{k}={1e6 * v / args.steps:.1f}" for k, v in seg.items()), file=sys.stderr, flush=True)
 
@@ -706,13 +710,16 @@ def main():
     unique_blocks = int(np.unique(used).size)
     block_bytes = 2 * bs * c.num_kv_heads * c.head_dim * c.elem_bytes
 
-    timed = range(args.warmup, nsteps)
-    dec_ms = [ev0[k].elapsed_time(ev1[k]) for k in timed]
+    timed = range(args.warmup, args.warmup + args.steps)
     lens_t = [step_lens[k] for k in timed]
     kv_bytes = [decode_kv_bytes(L, c.num_kv_heads, c.head_dim, c.elem_bytes) for L in lens_t]
+    # roofline: the marked decode calls, each timed by its own events
+    dec_ms = [ev0[k].elapsed_time(ev1[k]) for k in marked]
+    lens_m = [step_lens[k] for k in marked]
+    kv_bytes_m = [decode_kv_bytes(L, c.num_kv_heads, c.head_dim, c.elem_bytes) for L in lens_m]
     alg_bytes = [decode_algorithmic_bytes(L, c.num_q_heads, c.num_kv_heads, c.head_dim, bs, c.elem_bytes)
-                 for L in lens_t]
-    flops = [decode_flops(L, c.num_q_heads, c.head_dim) for L in lens_t]
+                 for L in lens_m]
+    flops = [decode_flops(L, c.num_q_heads, c.head_dim) for L in lens_m]
     mean_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
     achieved = (sum(alg_bytes) / len(alg_bytes)) / mean_dec_s
     ms_per_step = elapsed / args.steps * 1e3
@@ -747,7 +754,8 @@ def main():
         "tokens_per_s": round(S * args.steps / elapsed, 1),
         "pct_hbm_peak_whole_step": round(100.0 * value * 1e9 / HBM_PEAK, 2),
         "decode_call_us": round(mean_dec_s * 1e6, 2),
-        "decode_kv_gbps": round((sum(kv_bytes) / len(kv_bytes)) / mean_dec_s / 1e9, 2),
+        "decode_kv_gbps": round((sum(kv_bytes_m) / len(kv_bytes_m)) / mean_dec_s / 1e9, 2),
+        "decode_calls_marked": len(dec_ms),
         "decode_tflops": round((sum(flops) / len(flops)) / mean_dec_s / 1e12, 2),
         "cow_pairs": n_cow_total,
         "host_us_per_step": round(1e6 * sum(host_s[k] for k in timed) / args.steps, 1),
