@@ -110,7 +110,7 @@ struct StageLayout {
 // issued into the stage step st - 1 used (all modulo kStages); the stages in
 // between are landing.
 constexpr int kStages = 8;
-constexpr int kAhead = kStages - 1;
+constexpr int kAhead = kStages - 2;
 template <int D>
 struct PrefillSmem {
   u32x4 stage[kStages][StageLayout<D>::kStageBytes / 16];
@@ -127,11 +127,12 @@ __device__ __forceinline__ int vswz(int d) {
   return (d * n / 8) % n;
 }
 
-// s_waitcnt with vmcnt(n), lgkmcnt(0) and no wait on export counts.
+// s_waitcnt with vmcnt(n), lgkmcnt(0) and no wait on export counts (the
+// 6-bit vmcnt field is split: bits 3:0 and 15:14).
 template <int kN>
 __device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(kN >= 0 && kN < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(kN | (0x7 << 4));
+  static_assert(kN >= 0 && kN < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | (0x7 << 4));
 }
 
 // Workgroup barrier after this wave's LDS accesses and all but its newest kN
@@ -371,8 +372,8 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   }
   if (kAhead < nsteps) ids.read(sm.ids, kAhead * kTiles);
   const bool tail = nsteps * kKeys > L;  // the last step reaches past the context end
-  // stages 0 and 1 landed; steps 2 .. min(kAhead, nsteps) - 1 may be in flight
-  barrier_after_steps<kPer, kAhead - 2>((nsteps < kAhead ? nsteps : kAhead) - 2);
+  // stages 0..2 landed; steps 3 .. min(kAhead, nsteps) - 1 may be in flight
+  barrier_after_steps<kPer, kAhead - 3>((nsteps < kAhead ? nsteps : kAhead) - 3);
   if (nsteps == 1 && tail) {
     zero_v_tail<D, BS>(sm.stage[0], 0, L);
     stage_barrier<0>();
@@ -407,7 +408,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
       load_stage<D, BS>(sm.stage[nxa], plan, stride, ids);
       if (st + kAhead + 1 < nsteps) {
         if ((st + kAhead + 1) * kTiles >= chunk_base + kIdChunk) {
-          // Every read of the staged ids so far happened before the last barrier.
+          __syncthreads();  // every wave has read the ids of its steps so far
           chunk_base += kIdChunk;
           fill_ids(a, table, chunk_base, nblk, sm.ids);
           __syncthreads();
@@ -415,7 +416,8 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         ids.read(sm.ids, (st + kAhead + 1) * kTiles - chunk_base);  // its loads are issued a step later
       }
     }
-    if (tail && st + 1 == nsteps - 1) zero_v_tail<D, BS>(sm.stage[nx1], (st + 1) * kKeys, L);
+    const bool zero = tail && st + 1 == nsteps - 1;  // stage st + 1 landed at the last barrier
+    if (zero) zero_v_tail<D, BS>(sm.stage[nx1], (st + 1) * kKeys, L);
 
     // ---- row max of step st (raw scores; the scale is positive, so it
     // commutes with the max and is folded into the exponent below).
@@ -469,8 +471,15 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // stage st + 2 landed; steps st + 3 .. min(st + kAhead, nsteps - 1) may be in flight
-    barrier_after_steps<kPer, kAhead - 2>((nsteps - 1 - st < kAhead ? nsteps - 1 - st : kAhead) - 2);
+    // A barrier closes every second step (odd st): stages up to st + 3 have
+    // landed, steps st + 4 .. min(st + kAhead, nsteps - 1) may be in flight.
+    // Between barriers the waves run up to two steps apart: a stage is
+    // reloaded kStages - kAhead = 2 steps after its last reader, and the QK
+    // product of step st + 1 never reads past stage st + 3.
+    if (st & 1)
+      barrier_after_steps<kPer, kAhead - 3>((nsteps - 1 - st < kAhead ? nsteps - 1 - st : kAhead) - 3);
+    else if (zero)
+      stage_barrier<63>();  // publish the zeroed slots before PV(st + 1)
   };
 
   float16v s0 = qk(reinterpret_cast<const char*>(sm.stage[0])), s1;
