@@ -110,7 +110,12 @@ struct StageLayout {
 // issued into the stage step st - 1 used (all modulo kStages); the stages in
 // between are landing.
 constexpr int kStages = 8;
-constexpr int kAhead = kStages - 2;
+// A workgroup barrier closes every kBarrierEvery-th step; between barriers
+// the waves may run up to that many steps apart, so a stage may be reloaded
+// only that many steps after its last reader.
+constexpr int kBarrierEvery = 3;
+constexpr int kAhead = kStages - kBarrierEvery;
+static_assert(kAhead >= kBarrierEvery + 1, "the stage read next must have landed at each barrier");
 template <int D>
 struct PrefillSmem {
   u32x4 stage[kStages][StageLayout<D>::kStageBytes / 16];
@@ -372,8 +377,9 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   }
   if (kAhead < nsteps) ids.read(sm.ids, kAhead * kTiles);
   const bool tail = nsteps * kKeys > L;  // the last step reaches past the context end
-  // stages 0..2 landed; steps 3 .. min(kAhead, nsteps) - 1 may be in flight
-  barrier_after_steps<kPer, kAhead - 3>((nsteps < kAhead ? nsteps : kAhead) - 3);
+  // stages 0 .. kBarrierEvery landed; later steps up to min(kAhead, nsteps) - 1 may be in flight
+  constexpr int kInFlight = kAhead - kBarrierEvery - 1;  // steps a barrier lets stay in flight
+  barrier_after_steps<kPer, kInFlight>((nsteps < kAhead ? nsteps : kAhead) - kBarrierEvery - 1);
   if (nsteps == 1 && tail) {
     zero_v_tail<D, BS>(sm.stage[0], 0, L);
     stage_barrier<0>();
@@ -471,13 +477,12 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // A barrier closes every second step (odd st): stages up to st + 3 have
-    // landed, steps st + 4 .. min(st + kAhead, nsteps - 1) may be in flight.
-    // Between barriers the waves run up to two steps apart: a stage is
-    // reloaded kStages - kAhead = 2 steps after its last reader, and the QK
-    // product of step st + 1 never reads past stage st + 3.
-    if (st & 1)
-      barrier_after_steps<kPer, kAhead - 3>((nsteps - 1 - st < kAhead ? nsteps - 1 - st : kAhead) - 3);
+    // The barrier closing step st (every kBarrierEvery-th step) leaves
+    // stages up to st + kBarrierEvery + 1 landed, which the QK products of
+    // the steps until the next barrier read; steps after that up to
+    // min(st + kAhead, nsteps - 1) may be in flight.
+    if ((st + 1) % kBarrierEvery == 0)
+      barrier_after_steps<kPer, kInFlight>((nsteps - 1 - st < kAhead ? nsteps - 1 - st : kAhead) - kBarrierEvery - 1);
     else if (zero)
       stage_barrier<63>();  // publish the zeroed slots before PV(st + 1)
   };
