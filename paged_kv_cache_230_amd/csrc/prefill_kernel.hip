@@ -17,10 +17,12 @@
 //     lane pair (l, l+32).  All tiles of one (sequence, kv head) pair run on
 //     one XCD, so they share its L2.
 //   * Keys advance 32 per step.  The step's K and V block tiles are copied
-//     into an 8-stage LDS ring by direct global-to-LDS loads issued 7 steps
+//     into an 8-stage LDS ring by direct global-to-LDS loads issued 5 steps
 //     ahead, as permutations of the pool's 16-byte chunks (layouts at
 //     StageLayout); V slots past the context are zeroed in LDS, so unused
-//     slots of the last block never reach the products.
+//     slots of the last block never reach the products.  A workgroup
+//     barrier closes every third step only, so the waves need not run in
+//     lockstep.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the step's 32 keys (in slot
 //     order) in the rows, the wave's 32 query rows in the columns.  Lane l
 //     holds 16 scores of row l%32, keys 16(j/8)+8(l/32)+j%8, so a row's max
@@ -359,10 +361,10 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   for (int t = 0; t < kDimTiles; ++t) acc[t] = float16v{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Pipeline (see kStages): the loads of step st + kAhead are issued at the
-  // top of step st; the barrier closing step st waits for this wave's loads
-  // of step st + 2 (all later steps' may still be in flight) and so
-  // publishes stage st + 2 before step st + 1 reads its K.
+  // Pipeline (see kStages, kBarrierEvery): the loads of step st + kAhead are
+  // issued at the top of step st; a barrier waits for this wave's loads of
+  // the stages the QK products read before the next barrier (later steps'
+  // may still be in flight) and so publishes them.
   constexpr int kPer = StageLayout<D>::kPerThread;
   int chunk_base = 0;
   fill_ids(a, table, 0, nblk, sm.ids);
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
       load_stage<D, BS>(sm.stage[k], plan, stride, ids);
     }
   }
-  if (kAhead < nsteps) ids.read(sm.ids, kAhead * kTiles);
+  if (kAhead < nsteps) ids.read(sm.ids, kAhead * kTiles);  // for the loads issued in step 0
   const bool tail = nsteps * kKeys > L;  // the last step reaches past the context end
   // stages 0 .. kBarrierEvery landed; later steps up to min(kAhead, nsteps) - 1 may be in flight
   constexpr int kInFlight = kAhead - kBarrierEvery - 1;  // steps a barrier lets stay in flight
