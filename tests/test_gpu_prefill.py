@@ -1,5 +1,5 @@
 """Chunked-prefill attention on the GPU against the oracle: every kernel
-instantiation (head_dim 64/128 x block 16/32) and group sizes 1..128, ragged
+instantiation (head_dim 64/128 x block 16/32) and group sizes 1..256, ragged
 chunks (1 token, tile-sized, tile + tail) over histories from empty to
 several hundred tokens, the stress value distributions, NaN in unused pool
 slots, two consecutive chunks, and sampled rows of the full-size batch
@@ -9,14 +9,6 @@ Tolerance: the elementwise bound of ``helpers.assert_within_prefill_bound``
 (bf16 probabilities in the value product: u * mean_w|V| + u * |out|), plus
 the decode bar's 2e-3 absolute error."""
 
-
-def _check(run, w, out, k, what):
-    q = w.prefill_q(k)
-    ref = run.prefill_attention(q)
-    tables, lens = run.tables()
-    absv = run.v_pool & np.uint16(0x7FFF)  # |V|: clear the bf16 sign bit
-    A = oatt.prefill_attention(_storage(q), run.k_pool, absv, tables, lens, w.query_start())
-    assert_within_prefill_bound(out, ref, A, what)
 import numpy as np
 import pytest
 import torch
@@ -40,6 +32,15 @@ SHAPES = [  # (q heads, kv heads, head_dim, block size)
     (128, 1, 128, 16),  # G 128: two tokens per tile
     (256, 1, 64, 32),   # G 256: one token per tile
 ]
+
+
+def _check(run, w, out, k, what):
+    q = w.prefill_q(k)
+    ref = run.prefill_attention(q)
+    tables, lens = run.tables()
+    absv = run.v_pool & np.uint16(0x7FFF)  # |V|: clear the bf16 sign bit
+    A = oatt.prefill_attention(_storage(q), run.k_pool, absv, tables, lens, w.query_start())
+    assert_within_prefill_bound(out, ref, A, what)
 
 
 def _w(shape, variant="plain", **extra):
