@@ -1,0 +1,39 @@
+"""Host-side accounting in bench.py (CPU only): the algorithmic byte and flop
+counts behind the roofline figures, and the slot-waste comparison of paging
+against a contiguous max-length reservation."""
+import sys
+import os
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+import bench  # noqa: E402
+
+
+def test_decode_bytes_70b_32k_closed_form():
+    # 16 sequences of 32773 tokens (the first timed step), 64/8 heads, d 128, bs 16, bf16
+    lens = [32773] * 16
+    kv = 16 * 32773 * 8 * 128 * 2 * 2
+    assert bench.decode_kv_bytes(lens, 8, 128, 2) == kv
+    qo = 2 * 16 * 64 * 128 * 2
+    tables = 4 * 16 * 2049  # ceil(32773 / 16) entries per sequence
+    assert bench.decode_algorithmic_bytes(lens, 64, 8, 128, 16, 2) == kv + qo + tables + 4 * 16 == 2148466816
+
+
+def test_prefill_flops_equal_brute_force():
+    lens, chunks = [7, 20, 5], [3, 20, 1]
+    brute = 0
+    for L, C in zip(lens, chunks):
+        for p in range(L - C, L):  # token at position p reads keys 0..p
+            brute += 4 * 8 * 64 * (p + 1)
+    assert bench.prefill_flops(lens, chunks, 8, 64) == brute
+
+
+def test_paging_waste():
+    w = bench.paging_waste([17, 33, 64, 100], 16, 112)
+    assert w["paged_slots"] == (2 + 3 + 4 + 7) * 16 and w["tokens"] == 214
+    assert abs(w["paged_waste"] - 42 / 256) < 1e-5 and abs(w["reserved_waste"] - (448 - 214) / 448) < 1e-5
+    # whole-block paging wastes fewer than block_size slots per sequence
+    lens = [1, 16, 17, 1000, 4095]
+    w = bench.paging_waste(lens, 32, 4096)
+    assert w["paged_slots"] - w["tokens"] < 32 * len(lens)
+    assert bench.paging_waste([16, 32], 16, 32)["paged_waste"] == 0.0
