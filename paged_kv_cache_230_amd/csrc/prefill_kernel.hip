@@ -45,9 +45,8 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float float16v;
-// Plain vector types (not the HIP structs) so staged chunks stay in registers.
+// A 16-byte chunk as a plain vector type.
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
@@ -109,8 +108,8 @@ struct StageLayout {
 
 // Stage ring: during step st the PV product reads stage st, the QK product
 // of step st + 1 reads stage st + 1, and the loads of step st + kAhead are
-// issued into the stage step st - 1 used (all modulo kStages); the stages in
-// between are landing.
+// issued into the stage step st - kBarrierEvery used (all modulo kStages);
+// the stages in between are landing.
 constexpr int kStages = 8;
 // A workgroup barrier closes every kBarrierEvery-th step; between barriers
 // the waves may run up to that many steps apart, so a stage may be reloaded
