@@ -37,3 +37,13 @@ def test_paging_waste():
     w = bench.paging_waste(lens, 32, 4096)
     assert w["paged_slots"] - w["tokens"] < 32 * len(lens)
     assert bench.paging_waste([16, 32], 16, 32)["paged_waste"] == 0.0
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr and r.stdout == ""
