@@ -188,8 +188,6 @@ struct DecodeSmem {
   float o[kWaves][GMAX][D];  // per-wave accumulators of the current segment
   float m[kWaves][GMAX];
   float l[kWaves][GMAX];
-  float M[GMAX];    // merge: per-head maximum over pieces
-  float inv[GMAX];  // merge: 1 / weighted denominator
   int wave_sum[kWaves];
   int found_seq;
   int found_pre;
@@ -562,13 +560,18 @@ __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel
 // launch, so every partial written by the decode kernel is visible.
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
-  __shared__ DecodeSmem<BF16, D> sm;
   const int g = blockIdx.x;
   const int s = blockIdx.y;
   const int G = a.group;
   const int Hkv = a.num_kv_heads;
   const size_t head0 = static_cast<size_t>(s) * a.num_q_heads + static_cast<size_t>(g) * G;
-  const int L = clamp_len(a.context_lens[s], a.max_context_len);
+  // The length and the piece record are independent loads, issued together
+  // (the record is stale, and unused, for an empty sequence).
+  const int32_t* mt = a.meta + (static_cast<size_t>(s) * Hkv + g) * 2;
+  const int Lraw = a.context_lens[s];
+  const int first = mt[0];
+  const int npieces = mt[1];
+  const int L = clamp_len(Lraw, a.max_context_len);
   if (L == 0) {
     for (int e = threadIdx.x; e < G * D; e += kThreads) {
       if constexpr (BF16)
@@ -578,62 +581,65 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
     }
     return;
   }
-  const int32_t* mt = a.meta + (static_cast<size_t>(s) * Hkv + g) * 2;
-  const int first = mt[0];
-  const int npieces = mt[1];
   if (npieces <= 1) return;
   // Partial row of piece j: workgroup (first + j) of head g; slot 1 for the
   // first piece (it starts at the sequence's first block), slot 0 after.
   auto prow = [&](int j) { return ((first + j) * Hkv + g) * 2 + (j == 0 ? 1 : 0); };
 
-  // Phase 1: per head, M = max_j m_j and den = sum_j 2^(m_j - M) l_j; 16 threads per head.
-  {
-    const int h = threadIdx.x >> 4;
-    const int sub = threadIdx.x & 15;
-    const bool live = h < G;
-    float M = -INFINITY;
-    if (live)
-      for (int j = sub; j < npieces; j += 16) M = fmaxf(M, a.ws_m[static_cast<size_t>(prow(j)) * G + h]);
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
-    float den = 0.f;
-    if (live)
-      for (int j = sub; j < npieces; j += 16) {
-        const size_t r = static_cast<size_t>(prow(j)) * G + h;
-        den += __builtin_amdgcn_exp2f(a.ws_m[r] - M) * a.ws_l[r];
-      }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) den += __shfl_xor(den, off, 16);
-    if (live && sub == 0) {
-      sm.M[h] = M;
-      sm.inv[h] = 1.f / den;
-    }
-  }
-  __syncthreads();
-  // Phase 2: each thread owns 4 consecutive dims of one head.
+  // Each thread owns 4 consecutive dims of one head and merges the pieces
+  // kMergeChunk at a time: all of a chunk's loads (max, sum, accumulator
+  // slice) are issued before any is used, so a chunk costs one memory round
+  // trip.  Across chunks the running (max, sum, accumulator) is rescaled as
+  // in the online softmax.
+  constexpr int kMergeChunk = 8;
   for (int e = threadIdx.x * 4; e < G * D; e += kThreads * 4) {
     const int h = e / D;
     const int d = e - h * D;
-    const float M = sm.M[h];
+    float M = -INFINITY;
+    float den = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < npieces; ++j) {
-      const size_t r = static_cast<size_t>(prow(j)) * G + h;
-      const float f = __builtin_amdgcn_exp2f(a.ws_m[r] - M);
-      const float4 v = *reinterpret_cast<const float4*>(a.ws_acc + r * D + d);
-      acc.x += f * v.x;
-      acc.y += f * v.y;
-      acc.z += f * v.z;
-      acc.w += f * v.w;
-    }
-    const float inv = sm.inv[h];
-    const size_t o = (head0 + h) * D + d;
-    const float r4[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    for (int j0 = 0; j0 < npieces; j0 += kMergeChunk) {
+      float mj[kMergeChunk], lj[kMergeChunk];
+      float4 vj[kMergeChunk];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (BF16)
-        static_cast<uint16_t*>(a.out)[o + i] = f32_to_bf16_bits(r4[i]);
-      else
-        static_cast<float*>(a.out)[o + i] = r4[i];
+      for (int u = 0; u < kMergeChunk; ++u) {
+        const int j = j0 + u < npieces ? j0 + u : npieces - 1;
+        const size_t r = static_cast<size_t>(prow(j)) * G + h;
+        mj[u] = a.ws_m[r];
+        lj[u] = a.ws_l[r];
+        vj[u] = *reinterpret_cast<const float4*>(a.ws_acc + r * D + d);
+      }
+      float Mc = M;
+#pragma unroll
+      for (int u = 0; u < kMergeChunk; ++u)
+        if (j0 + u < npieces) Mc = fmaxf(Mc, mj[u]);
+      // Every piece holds at least one valid token, so Mc is finite.
+      const float c = __builtin_amdgcn_exp2f(M - Mc);
+      den *= c;
+      acc.x *= c;
+      acc.y *= c;
+      acc.z *= c;
+      acc.w *= c;
+#pragma unroll
+      for (int u = 0; u < kMergeChunk; ++u) {
+        const float f = j0 + u < npieces ? __builtin_amdgcn_exp2f(mj[u] - Mc) : 0.f;
+        den += f * lj[u];
+        acc.x += f * vj[u].x;
+        acc.y += f * vj[u].y;
+        acc.z += f * vj[u].z;
+        acc.w += f * vj[u].w;
+      }
+      M = Mc;
+    }
+    const float inv = 1.f / den;
+    const size_t o = (head0 + h) * D + d;
+    if constexpr (BF16) {
+      const uint32_t lo = f32_to_bf16_bits(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.y * inv)) << 16);
+      const uint32_t hi = f32_to_bf16_bits(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.w * inv)) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = make_uint2(lo, hi);
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
   }
 }
