@@ -85,6 +85,8 @@ def _pool_dims(k_cache, v_cache):
         raise ValueError(f"v_cache shape {tuple(v_cache.shape)} does not match k_cache {tuple(k_cache.shape)}")
     if x * k_cache.element_size() != 16:
         raise ValueError("k_cache last dim must span 16 bytes")
+    if not k_cache.is_cuda:
+        raise ValueError(f"k_cache must be a GPU tensor, got {k_cache.device}")
     return nb, H, d, bs
 
 
@@ -210,12 +212,15 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
     ``query_start[s] .. query_start[s+1]-1`` (its newest tokens, already
     appended); ``query_start``: int32 ``[S+1]`` on the device;
     ``max_query_len``: host bound on the chunk lengths."""
-    dev = q.device
-    T, Hq, d = q.shape
-    nb, H, _, bs, _ = k_cache.shape
+    nb, H, d, bs = _pool_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    _need(out, "out", k_cache.dtype, dev, 3)
+    T, Hq, dq = q.shape
+    if dq != d:
+        raise ValueError(f"q head_dim {dq} does not match the pools' {d}")
+    _need(context_lens, "context_lens", torch.int32, dev, 1)
     S = context_lens.shape[0]
-    _need(q, "q", k_cache.dtype, dev)
-    _need(out, "out", k_cache.dtype, dev)
     for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"), (query_start, "query_start")):
         _need(t, name, torch.int32, dev)
     if tuple(out.shape) != (T, Hq, d):
