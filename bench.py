@@ -5,8 +5,10 @@ One step = the whole hot path over one batch: host bookkeeping (slot and
 copy-on-write reservation in the block manager) staged to the GPU with
 pkv_bm_stage_step (one kernel reads the step's record from pinned memory
 and updates the device-resident block tables, lengths, slots and copy
-pairs), the copy-on-write block copy (when any), the cache append of one
-token per sequence, and decode attention with its log-sum-exp merge.  Consecutive steps are real decode
+pairs), the copy-on-write block copy (when any), then the cache append of
+one token per sequence and decode attention with its log-sum-exp merge in
+one call (paged_attention_decode_append; ``--separate-append`` runs them as
+two calls).  Consecutive steps are real decode
 steps: every sequence grows by one token per step, new blocks are taken at
 block boundaries.
 
@@ -56,6 +58,12 @@ def decode_algorithmic_bytes(lens, num_q_heads, num_kv_heads, head_dim, block_si
     qo = 2 * len(lens) * num_q_heads * head_dim * elem_bytes
     tables = 4 * sum(-(-int(L) // block_size) for L in lens)
     return kv + qo + tables + 4 * len(lens)
+
+
+def append_algorithmic_bytes(lens, num_kv_heads, head_dim, elem_bytes):
+    """Bytes of the one-token append of a decode step: each non-empty
+    sequence's new K and V rows read once and written once."""
+    return sum(1 for L in lens if int(L) > 0) * num_kv_heads * head_dim * 2 * 2 * elem_bytes
 
 
 def decode_kv_bytes(lens, num_kv_heads, head_dim, elem_bytes):
@@ -687,6 +695,9 @@ def main():
     ap.add_argument("--partition", type=int, default=0,
                     help="about this many tokens per decode workgroup (0 = one round of resident workgroups)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append with paged_kv_append, then paged_attention_decode (two calls) instead of "
+                         "paged_attention_decode_append")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences in the oracle sample (default: all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter calibration)")
@@ -792,12 +803,17 @@ def main():
         if n_cow:
             pkv.paged_kv_copy_blocks(cache.k_cache, cache.v_cache, pairs_d[:n_cow])
             n_cow_total += n_cow
-        pkv.paged_kv_append(step_k[k], step_v[k], cache.k_cache, cache.v_cache, slots_d)
+        if args.separate_append:
+            pkv.paged_kv_append(step_k[k], step_v[k], cache.k_cache, cache.v_cache, slots_d)
         t3 = time.perf_counter()
         if k in marked:
             ev0[k].record()
-        pkv.paged_attention_decode(out, step_q[k], cache.k_cache, cache.v_cache, tables_d, lens_d, max_len,
-                                   partition_size=P, workspace=workspace)
+        if args.separate_append:
+            pkv.paged_attention_decode(out, step_q[k], cache.k_cache, cache.v_cache, tables_d, lens_d, max_len,
+                                       partition_size=P, workspace=workspace)
+        else:
+            pkv.paged_attention_decode_append(out, step_q[k], step_k[k], step_v[k], cache.k_cache, cache.v_cache,
+                                              tables_d, lens_d, max_len, partition_size=P, workspace=workspace)
         if k in marked:
             ev1[k].record()
         t4 = time.perf_counter()
@@ -840,13 +856,15 @@ def main():
     lens_m = [step_lens[k] for k in marked]
     kv_bytes_m = [decode_kv_bytes(L, c.num_kv_heads, c.head_dim, c.elem_bytes) for L in lens_m]
     alg_bytes = [decode_algorithmic_bytes(L, c.num_q_heads, c.num_kv_heads, c.head_dim, bs, c.elem_bytes)
+                 + (0 if args.separate_append else append_algorithmic_bytes(L, c.num_kv_heads, c.head_dim,
+                                                                            c.elem_bytes))
                  for L in lens_m]
     flops = [decode_flops(L, c.num_q_heads, c.head_dim) for L in lens_m]
     mean_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
     achieved = (sum(alg_bytes) / len(alg_bytes)) / mean_dec_s
     ms_per_step = elapsed / args.steps * 1e3
     value = sum(kv_bytes) / elapsed / 1e9
-    traffic = load_traffic(w.name, P)
+    traffic = load_traffic(w.name, P) if not args.separate_append else None
 
     result = {
         "metric": METRIC,
@@ -883,7 +901,9 @@ def main():
         "host_us_per_step": round(1e6 * sum(host_s[k] for k in timed) / args.steps, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode (partition kernel + log-sum-exp merge)",
+            "kernel": ("paged_attention_decode (partition kernel + log-sum-exp merge)" if args.separate_append
+                       else "paged_attention_decode_append (partition kernel with the step's append + "
+                            "log-sum-exp merge)"),
             "achieved": round(achieved / 1e9, 2),
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",

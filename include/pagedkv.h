@@ -173,6 +173,33 @@ int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                                pkv_dtype dt, void* stream);
 
+/* Decode attention with the step's cache append folded in ([aitalk]     */
+/* step 3: each new token's K/V goes into the next slot of the sequence's */
+/* last block; step 2: the attention then reads that block through the   */
+/* table).  For each sequence s with L = context_lens[s] > 0, the K/V    */
+/* rows of the token at position L - 1 are first written from            */
+/* k_new[s] / v_new[s] into slot (L-1) % block_size of block              */
+/* block_tables[s][(L-1) / block_size] (skipped if that id is outside    */
+/* [0, num_blocks)), then out is computed exactly as by                  */
+/* paged_attention_decode.  Pools and out afterwards equal those of      */
+/* paged_kv_append with that slot mapping followed by                    */
+/* paged_attention_decode, bit for bit; one launch fewer per step.       */
+/*                                                                        */
+/* k_new, v_new  : device [num_seqs][num_kv_heads][head_dim], dtype dt,   */
+/*                 16-byte aligned, not null when num_seqs > 0            */
+/* k_cache, v_cache : written (one slot per sequence) and read            */
+/* The block holding position L - 1 must belong to sequence s alone      */
+/* (the block manager's append_slots and stage_step guarantee this by    */
+/* copy-on-write); every other argument, the workspace and the errors    */
+/* are as for paged_attention_decode.                                    */
+int32_t paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, pkv_dtype dt, void* stream);
+
 /* Workgroups per kv head that paged_attention_decode uses for these     */
 /* arguments on the current device, or a negative status.                 */
 int32_t paged_attention_workgroups_per_head(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,

@@ -78,6 +78,8 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const void* k_new;  // [S][Hkv][D] token appended at position L - 1, or null
+  const void* v_new;
   float* ws_acc;     // [N][2][G][D] partial accumulators (workgroup, slot, head)
   float* ws_m;       // [N][2][G] partial max (log2 domain)
   float* ws_l;       // [N][2][G] partial sum
@@ -225,11 +227,48 @@ __device__ __forceinline__ int block_scan(int v, int* total, DecodeSmem<BF16, D>
 // Slot 1 holds a piece that starts at its sequence's first block, slot 0 a
 // piece that starts inside the sequence.
 
+// Writes the K/V row of kv head g of the token at position L - 1 of
+// sequence s, taken from k_new/v_new [S][Hkv][D], into its pool slot: the
+// cache append, done by the workgroup that reads that slot.  The tile
+// formats are those of the pools: K [D/X][BS][X] (X = 16 bytes of
+// elements), V [D][BS].  A block id outside the pool skips the write.
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void append_last_token(const DecodeArgs& a, int s, int g, int L) {
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int X = 16 / EB;
+  const int pos = L - 1;
+  const int lb = pos / BS;
+  const int o = pos - lb * BS;
+  const int32_t blk = a.block_tables[static_cast<size_t>(s) * a.max_blocks_per_seq + lb];
+  if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) return;
+  const size_t tile = (static_cast<size_t>(blk) * a.num_kv_heads + g) * static_cast<size_t>(D) * BS;
+  const size_t src = (static_cast<size_t>(s) * a.num_kv_heads + g) * D;
+  const char* kn = static_cast<const char*>(a.k_new);
+  const char* vn = static_cast<const char*>(a.v_new);
+  char* kc = const_cast<char*>(static_cast<const char*>(a.k_cache));
+  char* vc = const_cast<char*>(static_cast<const char*>(a.v_cache));
+  for (int c = threadIdx.x; c < D / X; c += kThreads)
+    *reinterpret_cast<uint4*>(kc + (tile + (static_cast<size_t>(c) * BS + o) * X) * EB) =
+        *reinterpret_cast<const uint4*>(kn + (src + static_cast<size_t>(c) * X) * EB);
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    if constexpr (BF16)
+      reinterpret_cast<uint16_t*>(vc)[tile + static_cast<size_t>(d) * BS + o] =
+          reinterpret_cast<const uint16_t*>(vn)[src + d];
+    else
+      reinterpret_cast<uint32_t*>(vc)[tile + static_cast<size_t>(d) * BS + o] =
+          reinterpret_cast<const uint32_t*>(vn)[src + d];
+  }
+}
+
 // Blocks [lb0, lb1) of sequence s (length L) for kv head g.  When
 // `prow` < 0 the segment is the whole sequence and the output rows are
 // written; otherwise (max, sum, accumulator) go to partial row `prow`.
+// With `append`, the segment holds the sequence's last block and first
+// writes the appended token's K/V into it; the workgroup barrier that
+// follows the staging of the block ids orders those stores before every
+// wave's loads of the block (one workgroup, one compute unit and its L1).
 template <bool BF16, int D, int BS>
-__device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0, int lb1, int prow,
+__device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0, int lb1, int prow, bool append,
                                DecodeSmem<BF16, D>& sm) {
   constexpr int NT = D / 16;
   const int lane = threadIdx.x & 63;
@@ -372,6 +411,7 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
   // steps per block when BS = 32), loading step n+1 while computing step n.
   // Block ids come through LDS, kIdChunk at a time.
   constexpr int HALVES = BS / 16;
+  if (append) append_last_token<BF16, D, BS>(a, s, g, L);
   for (int c0 = 0; c0 < nblk; c0 += kIdChunk) {
     const int cn = nblk - c0 < kIdChunk ? nblk - c0 : kIdChunk;
     for (int i = threadIdx.x; i < cn; i += kThreads) {
@@ -541,7 +581,7 @@ __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel
     const int lb1 = static_cast<int>((b1 < static_cast<int64_t>(pre) + nb ? b1 : static_cast<int64_t>(pre) + nb) - pre);
     const bool whole = lb0 == 0 && lb1 == nb;
     const int prow = whole ? -1 : (b * 2 + (lb0 == 0 ? 1 : 0));
-    decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, sm);
+    decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, a.k_new != nullptr && lb1 == nb, sm);
     if (lb0 == 0 && threadIdx.x == 0) {
       // Workgroup (within this head) holding block x of the list: the largest
       // k' with k' T / Ng <= x.
@@ -963,12 +1003,19 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
                                        n * num_kv_heads).total);
 }
 
-int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
-                               int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dt,
-                               void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points: validation, workspace layout and launch.
+// k_new/v_new null: decode only; else the token at position L - 1 of each
+// sequence is appended from them first.
+int32_t decode_call(void* out, const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                    const void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dt, void* stream,
+                    const char* what) {
   if (int32_t e = check_common(head_dim, block_size, dt)) return e;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0)
@@ -992,6 +1039,8 @@ int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, co
     return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return pkv::fail(PKV_ERR_INVALID_ARG, "q, out and the pools must be 16-byte aligned");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
   if (partition_size < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "partition_size %d < 0", partition_size);
   if (static_cast<int64_t>(num_seqs) * max_blocks_per_seq > INT32_MAX)
     return pkv::fail(PKV_ERR_INVALID_ARG, "num_seqs * max_blocks_per_seq exceeds the int32 range");
@@ -1011,6 +1060,8 @@ int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, co
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.k_new = k_new;
+  a.v_new = v_new;
   char* ws = static_cast<char*>(workspace);
   a.meta = reinterpret_cast<int32_t*>(ws + wl.meta);
   a.ws_m = reinterpret_cast<float*>(ws + wl.m);
@@ -1037,7 +1088,34 @@ int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, co
     else
       dispatch_bs<false, 64>(a, block_size, st);
   }
-  return launch_status("paged_attention_decode");
+  return launch_status(what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                               int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dt,
+                               void* stream) {
+  return decode_call(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                     partition_size, workspace, workspace_bytes, dt, stream, "paged_attention_decode");
+}
+
+int32_t paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                      void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                      int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, pkv_dtype dt, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  return decode_call(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                     partition_size, workspace, workspace_bytes, dt, stream, "paged_attention_decode_append");
 }
 
 }  // extern "C"

@@ -22,7 +22,7 @@ def test_header_declares_the_hot_path():
     for must in ("paged_kv_append", "paged_kv_copy_blocks", "paged_attention_decode", "pkv_bm_create",
                  "pkv_bm_append_slots", "pkv_bm_fork", "pkv_bm_free_seq", "pkv_bm_block_tables"):
         assert must in names
-    assert len(names) == 43
+    assert len(names) == 44
 
 
 def test_library_exports_every_declared_symbol():
@@ -68,6 +68,26 @@ def test_host_validation_rejects_before_any_device_call():
     assert call(scale=float("nan")) == N.PKV_ERR_INVALID_ARG
     assert call(S=0) == 0
     assert call() == N.PKV_ERR_INVALID_ARG  # null pointers
+
+
+def test_decode_append_host_validation():
+    import paged_kv_cache_230_amd._native as N
+
+    null = C.c_void_p(0)
+    fake = C.c_void_p(256)  # aligned, never dereferenced: every call below fails validation first
+
+    def call(kn=fake, vn=fake, S=2, Hq=8, Hkv=2, d=128, bs=16, dt=N.PKV_BF16, others=fake):
+        return N.lib.paged_attention_decode_append(others, others, kn, vn, others, others, others, others, S, Hq, Hkv,
+                                                   d, bs, 10, 4, 64, 0.1, 0, others, 1 << 20, dt, null)
+
+    assert call(S=0, kn=null, vn=null, others=null) == 0
+    assert call(kn=null) == N.PKV_ERR_INVALID_ARG
+    assert call(vn=null) == N.PKV_ERR_INVALID_ARG
+    assert call(kn=C.c_void_p(258)) == N.PKV_ERR_INVALID_ARG
+    assert "k_new" in N.last_error()
+    assert call(Hq=32) == N.PKV_ERR_UNSUPPORTED  # G = 16 > 8 for bf16
+    assert call(d=96) == N.PKV_ERR_UNSUPPORTED
+    assert call(others=null) == N.PKV_ERR_INVALID_ARG
 
 
 def test_prefill_host_validation():

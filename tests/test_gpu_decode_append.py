@@ -1,0 +1,149 @@
+"""paged_attention_decode_append: the step's cache append folded into the
+decode kernel.  Its pools and outputs must equal, bit for bit, those of
+paged_kv_append (at the slot of position L - 1) followed by
+paged_attention_decode, and its outputs must match the oracle within the
+decode tolerances.  Unused slots hold NaN, so a token the fused kernel
+failed to write would show up in the output and in the pool comparison."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import assert_close, product_cache, say, storage_np
+from oracle.runner import OracleRun
+from workloads import Workload
+
+import oracle.attention as oatt
+import oracle.pool as opool
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(dt, d, bs) for dt in ("f32", "bf16") for d in (64, 128) for bs in (16, 32)]
+
+
+def _bits_equal(a, b):
+    return np.array_equal(storage_np(a).view(np.uint8), storage_np(b).view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype,d,bs", SHAPES, ids=[f"{a}-d{b}-bs{c}" for a, b, c in SHAPES])
+@pytest.mark.parametrize("part", [0, 48 * 32])
+def test_every_instantiation_matches_append_then_decode(dtype, d, bs, part):
+    import paged_kv_cache_230_amd as pkv
+
+    say(f"case decode_append {dtype} d{d} bs{bs} partition {part}")
+    lens = [1, bs - 1, 0, bs, bs + 1, 7 * bs + 3, 40 * bs + 5, 3]
+    Hq, Hkv = 8, 2
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    g = torch.Generator().manual_seed(7 * d + bs)
+    S = len(lens)
+    nb = sum(-(-L // bs) for L in lens) + 5
+    perm = torch.randperm(nb, generator=g).numpy()
+    maxb = max(-(-L // bs) for L in lens)
+    tables = np.full((S, maxb), -1, np.int32)
+    used = 0
+    for s, L in enumerate(lens):
+        n = -(-L // bs)
+        tables[s, :n] = perm[used:used + n]
+        used += n
+    slot = lambda s, t: int(tables[s, t // bs]) * bs + t % bs  # noqa: E731
+    hist = [(s, t) for s, L in enumerate(lens) for t in range(L - 1)]  # cached before the step
+    std = 1.0 if dtype == "f32" else 128 ** -0.5
+    kh = (torch.randn(len(hist), Hkv, d, generator=g) * std).to(tdt)
+    vh = (torch.randn(len(hist), Hkv, d, generator=g) * std).to(tdt)
+    kn = (torch.randn(S, Hkv, d, generator=g) * std).to(tdt)
+    vn = (torch.randn(S, Hkv, d, generator=g) * std).to(tdt)
+    q = (torch.randn(S, Hq, d, generator=g) * std * (1.0 if dtype == "f32" else 8.0)).to(tdt)
+
+    kA, vA = pkv.new_pools(nb, Hkv, d, bs, tdt)
+    kA.fill_(float("nan"))
+    vA.fill_(float("nan"))
+    if hist:
+        pkv.paged_kv_append(kh.cuda(), vh.cuda(), kA, vA,
+                            torch.tensor([slot(s, t) for s, t in hist], dtype=torch.int32).cuda())
+    kB, vB = kA.clone(), vA.clone()
+    tab = torch.from_numpy(tables).cuda()
+    ln = torch.tensor(lens, dtype=torch.int32).cuda()
+    new_slots = torch.tensor([slot(s, L - 1) if L else -1 for s, L in enumerate(lens)], dtype=torch.int32).cuda()
+
+    outA = torch.full((S, Hq, d), float("nan"), dtype=tdt, device="cuda")
+    pkv.paged_kv_append(kn.cuda(), vn.cuda(), kA, vA, new_slots)
+    pkv.paged_attention_decode(outA, q.cuda(), kA, vA, tab, ln, max(lens), partition_size=part)
+    outB = torch.full_like(outA, float("nan"))
+    pkv.paged_attention_decode_append(outB, q.cuda(), kn.cuda(), vn.cuda(), kB, vB, tab, ln, max(lens),
+                                      partition_size=part)
+    torch.cuda.synchronize()
+    assert _bits_equal(kA, kB) and _bits_equal(vA, vB), "pools differ from append + decode"
+    assert _bits_equal(outA, outB), "outputs differ from append + decode"
+
+    # oracle: all L tokens of every sequence in an oracle pool, then decode
+    sd = np.float32 if dtype == "f32" else np.uint16
+    ok, ov = opool.new_pools(nb, Hkv, d, bs, sd)
+
+    def st(t):
+        return t.numpy() if t.dtype == torch.float32 else t.view(torch.int16).numpy().view(np.uint16)
+
+    live = [s for s, L in enumerate(lens) if L]
+    opool.append(ok, ov, np.concatenate([st(kh), st(kn)[live]]), np.concatenate([st(vh), st(vn)[live]]),
+                 np.array([slot(s, t) for s, t in hist] + [slot(s, lens[s] - 1) for s in live], np.int64))
+    ref = oatt.decode_attention(st(q), ok, ov, tables, np.array(lens))
+    assert_close(outB, ref, dtype, f"decode_append {dtype} d{d} bs{bs} P{part}")
+    assert not storage_np(outB)[lens.index(0)].any(), "empty sequence must give a zero row"
+
+
+def _two_paths(w, steps):
+    """Run `steps` decode steps of workload w through both paths from the
+    same bookkeeping: path A appends then decodes, path B calls the fused
+    entry point.  Returns the last step's outputs and the cache of path A."""
+    import paged_kv_cache_230_amd as pkv
+
+    c = w.config
+    say(f"case decode_append {w.name}: building the cache")
+    cache = product_cache(w)
+    kB, vB = cache.k_cache.clone(), cache.v_cache.clone()
+    bs = c.block_size
+    for k in range(steps):
+        kn, vn = w.kv(("step", k))
+        kn, vn = kn.cuda(), vn.cuda()
+        slots, pairs = cache.bm.append_slots(w.decode_seqs, [1] * w.num_seqs)
+        tables, lens, th, lh = cache.tables(w.decode_seqs)
+        expect = [int(th[i, (L - 1) // bs]) * bs + (L - 1) % bs for i, L in enumerate(lh)]
+        assert slots.tolist() == expect, "the block manager's slot is not position L - 1"
+        if pairs.shape[0]:
+            pd = torch.from_numpy(pairs.copy()).cuda()
+            pkv.paged_kv_copy_blocks(cache.k_cache, cache.v_cache, pd)
+            pkv.paged_kv_copy_blocks(kB, vB, pd)
+        q = w.q(k).cuda()
+        max_len = int(lh.max())
+        outA = torch.empty_like(q)
+        pkv.paged_kv_append(kn, vn, cache.k_cache, cache.v_cache, torch.from_numpy(slots.copy()).cuda())
+        pkv.paged_attention_decode(outA, q, cache.k_cache, cache.v_cache, tables, lens, max_len)
+        outB = torch.empty_like(q)
+        pkv.paged_attention_decode_append(outB, q, kn, vn, kB, vB, tables, lens, max_len)
+        torch.cuda.synchronize()
+        say(f"  step {k}: {pairs.shape[0]} copy pairs, max_len {max_len}")
+        assert torch.equal(outA.view(torch.int16), outB.view(torch.int16)), f"step {k}: outputs differ"
+    assert torch.equal(cache.k_cache.view(torch.int16), kB.view(torch.int16)), "K pools differ"
+    assert torch.equal(cache.v_cache.view(torch.int16), vB.view(torch.int16)), "V pools differ"
+    return outB, cache
+
+
+def test_70b_32k_full_size_bitwise_and_sampled_oracle():
+    """The 70B-shaped 32k layer at full size in the default launch; sampled
+    sequences against the oracle from their logical tokens."""
+    w = Workload("c3_70b_32k_bf16")
+    out, _ = _two_paths(w, steps=2)
+    run = OracleRun(w, materialize=False)
+    run.step(0)
+    run.step(1)
+    q = w.q(1)
+    for s in (0, 15):
+        assert_close(out[s].cpu(), run.logical_attention(q, s), "bf16", f"70B 32k seq {s} step 1")
+
+
+def test_mixed_bs32_full_size_bitwise():
+    _two_paths(Workload("c5_mixed_bs32_bf16"), steps=3)
+
+
+def test_prefix_sharing_with_copy_on_write_bitwise():
+    """400 sequences over a shared prefix: the first step copies the shared
+    partial blocks before the fused append writes into the copies."""
+    _two_paths(Workload("c4_prefix_bf16"), steps=2)
