@@ -193,6 +193,9 @@ struct DecodeSmem {
   int wave_sum[kWaves];
   int found_seq;
   int found_pre;
+  // k_new / v_new of an appending call, parked here so the kernel does not
+  // hold them in scalar registers through the step loop
+  const void* append_src[2];
   int ids[kIdChunk];  // block ids of the current chunk of the segment
 };
 
@@ -227,36 +230,59 @@ __device__ __forceinline__ int block_scan(int v, int* total, DecodeSmem<BF16, D>
 // Slot 1 holds a piece that starts at its sequence's first block, slot 0 a
 // piece that starts inside the sequence.
 
-// Writes the K/V row of kv head g of the token at position L - 1 of
-// sequence s, taken from k_new/v_new [S][Hkv][D], into its pool slot: the
-// cache append, done by the workgroup that reads that slot.  The tile
-// formats are those of the pools: K [D/X][BS][X] (X = 16 bytes of
-// elements), V [D][BS].  A block id outside the pool skips the write.
+// The cache append done by the decode kernel: the K/V row of kv head g of
+// the token at position L - 1 of sequence s, from k_new/v_new
+// [S][Hkv][D], goes into its pool slot, written by the workgroup that
+// reads that slot.  The tile formats are those of the pools: K
+// [D/X][BS][X] (X = 16 bytes of elements), V [D][BS].  A block id outside
+// the pool skips the write.  The loads (table entry, one K chunk or one V
+// element per thread) are independent and issued together with the staging
+// of the segment's block ids, so they add no round trip of their own.
+template <bool BF16, int D>
+struct AppendRow {
+  uint4 k;     // K chunk `threadIdx.x` (threads < D / X)
+  uint32_t v;  // V element `threadIdx.x` (threads < D)
+  int32_t blk;
+};
+
 template <bool BF16, int D, int BS>
-__device__ __forceinline__ void append_last_token(const DecodeArgs& a, int s, int g, int L) {
+__device__ __forceinline__ AppendRow<BF16, D> append_load(const DecodeArgs& a, const void* k_new, const void* v_new,
+                                                          int s, int g, int L) {
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int X = 16 / EB;
-  const int pos = L - 1;
-  const int lb = pos / BS;
-  const int o = pos - lb * BS;
-  const int32_t blk = a.block_tables[static_cast<size_t>(s) * a.max_blocks_per_seq + lb];
-  if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) return;
-  const size_t tile = (static_cast<size_t>(blk) * a.num_kv_heads + g) * static_cast<size_t>(D) * BS;
+  static_assert(D <= kThreads, "one V element per thread");
+  AppendRow<BF16, D> r;
+  r.blk = a.block_tables[static_cast<size_t>(s) * a.max_blocks_per_seq + (L - 1) / BS];
   const size_t src = (static_cast<size_t>(s) * a.num_kv_heads + g) * D;
-  const char* kn = static_cast<const char*>(a.k_new);
-  const char* vn = static_cast<const char*>(a.v_new);
+  const int t = threadIdx.x;
+  r.k = make_uint4(0, 0, 0, 0);
+  r.v = 0;
+  if (t < D / X) r.k = *reinterpret_cast<const uint4*>(static_cast<const char*>(k_new) + (src + t * X) * EB);
+  if (t < D) {
+    if constexpr (BF16)
+      r.v = static_cast<const uint16_t*>(v_new)[src + t];
+    else
+      r.v = static_cast<const uint32_t*>(v_new)[src + t];
+  }
+  return r;
+}
+
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void append_store(const DecodeArgs& a, const AppendRow<BF16, D>& r, int g, int L) {
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int X = 16 / EB;
+  if (static_cast<unsigned>(r.blk) >= static_cast<unsigned>(a.num_blocks)) return;
+  const int o = (L - 1) % BS;
+  const size_t tile = (static_cast<size_t>(r.blk) * a.num_kv_heads + g) * static_cast<size_t>(D) * BS;
   char* kc = const_cast<char*>(static_cast<const char*>(a.k_cache));
   char* vc = const_cast<char*>(static_cast<const char*>(a.v_cache));
-  for (int c = threadIdx.x; c < D / X; c += kThreads)
-    *reinterpret_cast<uint4*>(kc + (tile + (static_cast<size_t>(c) * BS + o) * X) * EB) =
-        *reinterpret_cast<const uint4*>(kn + (src + static_cast<size_t>(c) * X) * EB);
-  for (int d = threadIdx.x; d < D; d += kThreads) {
+  const int t = threadIdx.x;
+  if (t < D / X) *reinterpret_cast<uint4*>(kc + (tile + (static_cast<size_t>(t) * BS + o) * X) * EB) = r.k;
+  if (t < D) {
     if constexpr (BF16)
-      reinterpret_cast<uint16_t*>(vc)[tile + static_cast<size_t>(d) * BS + o] =
-          reinterpret_cast<const uint16_t*>(vn)[src + d];
+      reinterpret_cast<uint16_t*>(vc)[tile + static_cast<size_t>(t) * BS + o] = static_cast<uint16_t>(r.v);
     else
-      reinterpret_cast<uint32_t*>(vc)[tile + static_cast<size_t>(d) * BS + o] =
-          reinterpret_cast<const uint32_t*>(vn)[src + d];
+      reinterpret_cast<uint32_t*>(vc)[tile + static_cast<size_t>(t) * BS + o] = r.v;
   }
 }
 
@@ -264,9 +290,9 @@ __device__ __forceinline__ void append_last_token(const DecodeArgs& a, int s, in
 // `prow` < 0 the segment is the whole sequence and the output rows are
 // written; otherwise (max, sum, accumulator) go to partial row `prow`.
 // With `append`, the segment holds the sequence's last block and first
-// writes the appended token's K/V into it; the workgroup barrier that
-// follows the staging of the block ids orders those stores before every
-// wave's loads of the block (one workgroup, one compute unit and its L1).
+// writes the appended token's K/V into it; the workgroup barrier after the
+// staging of the block ids orders those stores before every wave's loads
+// of the block (one workgroup: one compute unit and its L1).
 template <bool BF16, int D, int BS>
 __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0, int lb1, int prow, bool append,
                                DecodeSmem<BF16, D>& sm) {
@@ -411,13 +437,27 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
   // steps per block when BS = 32), loading step n+1 while computing step n.
   // Block ids come through LDS, kIdChunk at a time.
   constexpr int HALVES = BS / 16;
-  if (append) append_last_token<BF16, D, BS>(a, s, g, L);
-  for (int c0 = 0; c0 < nblk; c0 += kIdChunk) {
+  auto stage_ids = [&](int c0) {
     const int cn = nblk - c0 < kIdChunk ? nblk - c0 : kIdChunk;
     for (int i = threadIdx.x; i < cn; i += kThreads) {
       const int b = tbl[c0 + i];
       sm.ids[i] = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks) ? b : 0;
     }
+  };
+  // The first chunk's ids are staged before the loop, so the append (its
+  // loads issued with them, its stores after) ends before the step loop.
+  if (append) {
+    const void* kn = sm.append_src[0];
+    const void* vn = sm.append_src[1];
+    const AppendRow<BF16, D> arow = append_load<BF16, D, BS>(a, kn, vn, s, g, L);
+    stage_ids(0);
+    append_store<BF16, D, BS>(a, arow, g, L);
+  } else {
+    stage_ids(0);
+  }
+  for (int c0 = 0; c0 < nblk; c0 += kIdChunk) {
+    const int cn = nblk - c0 < kIdChunk ? nblk - c0 : kIdChunk;
+    if (c0 > 0) stage_ids(c0);
     __syncthreads();
     Step<BF16, D> st, nxt;
     const void* kt = nullptr;
@@ -533,6 +573,11 @@ __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel
   const int b = blockIdx.x;
   const int g = b % Hkv;
   const int k = b / Hkv;
+  const bool appending = a.k_new != nullptr;
+  if (threadIdx.x == 0) {
+    sm.append_src[0] = a.k_new;
+    sm.append_src[1] = a.v_new;
+  }  // ordered before the reads by the barriers of the length scans
 
   // Total blocks per head.
   int T = 0;
@@ -581,7 +626,7 @@ __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel
     const int lb1 = static_cast<int>((b1 < static_cast<int64_t>(pre) + nb ? b1 : static_cast<int64_t>(pre) + nb) - pre);
     const bool whole = lb0 == 0 && lb1 == nb;
     const int prow = whole ? -1 : (b * 2 + (lb0 == 0 ? 1 : 0));
-    decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, a.k_new != nullptr && lb1 == nb, sm);
+    decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, appending && lb1 == nb, sm);
     if (lb0 == 0 && threadIdx.x == 0) {
       // Workgroup (within this head) holding block x of the list: the largest
       // k' with k' T / Ng <= x.
@@ -685,6 +730,34 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Writes 16-byte chunk c of kv head h of one token's K/V row (rows of
+// k_new/v_new are [num_kv_heads][head_dim]) into pool slot `slot`.
+template <int EB>
+__device__ __forceinline__ void write_row_chunk(const char* __restrict__ k_row, const char* __restrict__ v_row,
+                                                char* __restrict__ k_cache, char* __restrict__ v_cache, int64_t slot,
+                                                int h, int c, int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size) {
+  constexpr int X = 16 / EB;
+  const int64_t b = slot / block_size;
+  const int o = static_cast<int>(slot - b * block_size);
+  const int64_t src = (static_cast<int64_t>(h) * head_dim + static_cast<int64_t>(c) * X) * EB;
+  const uint4 kv = *reinterpret_cast<const uint4*>(k_row + src);
+  const uint4 vv = *reinterpret_cast<const uint4*>(v_row + src);
+  const int64_t tile = (b * num_kv_heads + h) * static_cast<int64_t>(head_dim) * block_size;
+  *reinterpret_cast<uint4*>(k_cache + ((tile + (static_cast<int64_t>(c) * block_size + o) * X) * EB)) = kv;
+  const int64_t vdst = tile + static_cast<int64_t>(c) * X * block_size + o;
+  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+  if constexpr (EB == 2) {
+    uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vc[vdst + static_cast<int64_t>(i) * block_size] = static_cast<uint16_t>(w[i / 2] >> (16 * (i & 1)));
+  } else {
+    uint32_t* vc = reinterpret_cast<uint32_t*>(v_cache);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vc[vdst + static_cast<int64_t>(i) * block_size] = w[i];
+  }
+}
+
 // Cache append: one thread per (token, kv head, 16-byte chunk of head_dim).
 template <int EB>
 __global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ k_new, const char* __restrict__ v_new,
@@ -692,35 +765,46 @@ __global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ k_
                                                      const int32_t* __restrict__ slot_mapping, int64_t total,
                                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                                      int32_t num_blocks) {
-  constexpr int X = 16 / EB;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int nch = head_dim / X;
+  const int nch = head_dim / (16 / EB);
   const int c = static_cast<int>(idx % nch);
   const int64_t th = idx / nch;
   const int h = static_cast<int>(th % num_kv_heads);
   const int64_t t = th / num_kv_heads;
   const int32_t slot = slot_mapping[t];
   if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(num_blocks) * block_size) return;
-  const int64_t b = slot / block_size;
-  const int o = slot - static_cast<int32_t>(b) * block_size;
-  const int64_t src = ((t * num_kv_heads + h) * head_dim + static_cast<int64_t>(c) * X) * EB;
-  const uint4 kv = *reinterpret_cast<const uint4*>(k_new + src);
-  const uint4 vv = *reinterpret_cast<const uint4*>(v_new + src);
-  const int64_t tile = (b * num_kv_heads + h) * static_cast<int64_t>(head_dim) * block_size;
-  *reinterpret_cast<uint4*>(k_cache + ((tile + (static_cast<int64_t>(c) * block_size + o) * X) * EB)) = kv;
-  const int64_t vdst = tile + static_cast<int64_t>(c) * X * block_size + o;
-  if constexpr (EB == 2) {
-    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-    uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vc[vdst + static_cast<int64_t>(i) * block_size] = static_cast<uint16_t>(w[i / 2] >> (16 * (i & 1)));
-  } else {
-    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-    uint32_t* vc = reinterpret_cast<uint32_t*>(v_cache);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vc[vdst + static_cast<int64_t>(i) * block_size] = w[i];
-  }
+  const int64_t row = t * num_kv_heads * head_dim * EB;
+  write_row_chunk<EB>(k_new + row, v_new + row, k_cache, v_cache, slot, h, c, num_kv_heads, head_dim, block_size);
+}
+
+// The decode step's one-token append as its own launch: sequence s's row
+// goes to the slot of position L - 1 (L = its clamped context length),
+// found through its block table; L == 0 or a block id outside the pool
+// skips it.  One thread per (sequence, kv head, 16-byte chunk).
+template <int EB>
+__global__ __launch_bounds__(256) void append_last_kernel(const char* __restrict__ k_new,
+                                                          const char* __restrict__ v_new, char* __restrict__ k_cache,
+                                                          char* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ block_tables,
+                                                          const int32_t* __restrict__ context_lens, int64_t total,
+                                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                          int32_t num_blocks, int32_t max_blocks_per_seq,
+                                                          int32_t max_context_len) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int nch = head_dim / (16 / EB);
+  const int c = static_cast<int>(idx % nch);
+  const int64_t th = idx / nch;
+  const int h = static_cast<int>(th % num_kv_heads);
+  const int64_t s = th / num_kv_heads;
+  const int L = clamp_len(context_lens[s], max_context_len);
+  if (L == 0) return;
+  const int32_t blk = block_tables[s * max_blocks_per_seq + (L - 1) / block_size];
+  if (blk < 0 || blk >= num_blocks) return;
+  const int64_t slot = static_cast<int64_t>(blk) * block_size + (L - 1) % block_size;
+  const int64_t row = s * num_kv_heads * head_dim * EB;
+  write_row_chunk<EB>(k_new + row, v_new + row, k_cache, v_cache, slot, h, c, num_kv_heads, head_dim, block_size);
 }
 
 // Block copy: blockIdx.x = pair, blockIdx.y = 0 (K pool) or 1 (V pool).
@@ -1060,8 +1144,34 @@ int32_t decode_call(void* out, const void* q, const void* k_new, const void* v_n
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.k_new = k_new;
-  a.v_new = v_new;
+  // The append is folded into the decode kernel only when there is at most
+  // one appended (sequence, kv head) row per decode workgroup.  Each row's
+  // V part is head_dim two-byte stores (the V tile is dimension-major);
+  // many of them issued into the decode kernel's saturated read stream cost
+  // more than a separate launch (measured: +27 us on 256 sequences x 8 kv
+  // heads over 768 workgroups, against -4 us of launch saved on 16 x 8).
+  // Both ways write the same bytes.
+  const bool fold = k_new != nullptr && static_cast<int64_t>(num_seqs) <= wph;
+  if (k_new != nullptr && !fold) {
+    const int eb = dt == PKV_BF16 ? 2 : 4;
+    const int64_t total = static_cast<int64_t>(num_seqs) * num_kv_heads * (head_dim * eb / 16);
+    const int64_t blocks = (total + 255) / 256;
+    hipStream_t ast = static_cast<hipStream_t>(stream);
+    if (eb == 2)
+      append_last_kernel<2><<<dim3(static_cast<uint32_t>(blocks)), 256, 0, ast>>>(
+          static_cast<const char*>(k_new), static_cast<const char*>(v_new),
+          const_cast<char*>(static_cast<const char*>(k_cache)), const_cast<char*>(static_cast<const char*>(v_cache)),
+          block_tables, context_lens, total, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+          max_context_len);
+    else
+      append_last_kernel<4><<<dim3(static_cast<uint32_t>(blocks)), 256, 0, ast>>>(
+          static_cast<const char*>(k_new), static_cast<const char*>(v_new),
+          const_cast<char*>(static_cast<const char*>(k_cache)), const_cast<char*>(static_cast<const char*>(v_cache)),
+          block_tables, context_lens, total, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+          max_context_len);
+  }
+  a.k_new = fold ? k_new : nullptr;
+  a.v_new = fold ? v_new : nullptr;
   char* ws = static_cast<char*>(workspace);
   a.meta = reinterpret_cast<int32_t*>(ws + wl.meta);
   a.ws_m = reinterpret_cast<float*>(ws + wl.m);
