@@ -183,7 +183,10 @@ int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, co
 /* [0, num_blocks)), then out is computed exactly as by                  */
 /* paged_attention_decode.  Pools and out afterwards equal those of      */
 /* paged_kv_append with that slot mapping followed by                    */
-/* paged_attention_decode, bit for bit; one launch fewer per step.       */
+/* paged_attention_decode, bit for bit.  When num_seqs is at most the    */
+/* decode workgroups per kv head (paged_attention_workgroups_per_head),   */
+/* the decode kernel writes the rows itself, one launch fewer; otherwise  */
+/* a small append kernel runs first on the same stream.                  */
 /*                                                                        */
 /* k_new, v_new  : device [num_seqs][num_kv_heads][head_dim], dtype dt,   */
 /*                 16-byte aligned, not null when num_seqs > 0            */
