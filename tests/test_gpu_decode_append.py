@@ -1,9 +1,12 @@
-"""paged_attention_decode_append: the step's cache append folded into the
-decode kernel.  Its pools and outputs must equal, bit for bit, those of
-paged_kv_append (at the slot of position L - 1) followed by
-paged_attention_decode, and its outputs must match the oracle within the
-decode tolerances.  Unused slots hold NaN, so a token the fused kernel
-failed to write would show up in the output and in the pool comparison."""
+"""paged_attention_decode_append: the step's cache append and decode
+attention in one call (the decode kernel writes the rows itself when there
+is at most one appended row per decode workgroup, else a one-row append
+launch runs first; the cases below take both branches).  Its pools and
+outputs must equal, bit for bit, those of paged_kv_append (at the slot of
+position L - 1) followed by paged_attention_decode, and its outputs must
+match the oracle within the decode tolerances.  Unused slots hold NaN, so a
+token the call failed to write would show up in the output and in the pool
+comparison."""
 import numpy as np
 import pytest
 import torch
@@ -144,6 +147,51 @@ def test_mixed_bs32_full_size_bitwise():
 
 
 def test_prefix_sharing_with_copy_on_write_bitwise():
-    """400 sequences over a shared prefix: the first step copies the shared
-    partial blocks before the fused append writes into the copies."""
+    """400 sequences over a shared prefix (more than one appended row per
+    workgroup: the append launch runs first): the first step copies the
+    shared partial blocks before the append writes into the copies."""
     _two_paths(Workload("c4_prefix_bf16"), steps=2)
+
+
+@pytest.mark.parametrize("n_samples", [4, 16])
+def test_staged_steps_with_copy_on_write_match_two_calls(n_samples):
+    """The step as the benchmark runs it: bookkeeping staged to the device
+    buffers by pkv_bm_stage_step, copy-on-write copies, then the fused call.
+    Two pool sets from the same bookkeeping; 24 sequences fold the append
+    into the decode kernel, 128 take the separate append launch."""
+    import paged_kv_cache_230_amd as pkv
+    from test_gpu_stage import Staged
+
+    w = Workload("c4_prefix_bf16", variant="q64",
+                 overrides=dict(num_prompts=6 if n_samples == 4 else 8, n_samples=n_samples, num_blocks=3000))
+    c = w.config
+    say(f"case staged decode_append: {w.num_seqs} sequences")
+    cache = product_cache(w)
+    kB, vB = cache.k_cache.clone(), cache.v_cache.clone()
+    run = OracleRun(w)
+    n = w.num_seqs
+    st = Staged(n, maxb=200)
+    total_pairs = 0
+    for k in range(3):
+        n_cow, max_len = st.step(cache.bm, w.decode_seqs)
+        total_pairs += n_cow
+        if n_cow:
+            pkv.paged_kv_copy_blocks(cache.k_cache, cache.v_cache, st.pairs[:n_cow])
+            pkv.paged_kv_copy_blocks(kB, vB, st.pairs[:n_cow])
+        kn, vn = w.kv(("step", k))
+        kn, vn = kn.cuda(), vn.cuda()
+        q = w.q(k).cuda()
+        outA = torch.empty(n, c.num_q_heads, c.head_dim, dtype=c.torch_dtype, device="cuda")
+        pkv.paged_kv_append(kn, vn, cache.k_cache, cache.v_cache, st.slots)
+        pkv.paged_attention_decode(outA, q, cache.k_cache, cache.v_cache, st.tables, st.lens, max_len)
+        outB = torch.empty_like(outA)
+        pkv.paged_attention_decode_append(outB, q, kn, vn, kB, vB, st.tables, st.lens, max_len)
+        torch.cuda.synchronize()
+        run.step(k)
+        assert torch.equal(outA.view(torch.int16), outB.view(torch.int16)), f"step {k}: outputs differ"
+        assert_close(outB, run.attention(w.q(k)), "bf16", f"staged decode_append step {k}")
+    assert total_pairs > 0, "the workload must exercise copy-on-write"
+    assert torch.equal(cache.k_cache.view(torch.int16), kB.view(torch.int16)), "K pools differ"
+    assert torch.equal(cache.v_cache.view(torch.int16), vB.view(torch.int16)), "V pools differ"
+    wph = pkv.paged_attention_workgroups_per_head(n, c.num_kv_heads, c.head_dim, c.block_size, 200 * c.block_size)
+    say(f"  {n} sequences, {wph} workgroups per kv head: append {'folded' if n <= wph else 'launched first'}")
