@@ -195,3 +195,64 @@ def test_staged_steps_with_copy_on_write_match_two_calls(n_samples):
     assert torch.equal(cache.v_cache.view(torch.int16), vB.view(torch.int16)), "V pools differ"
     wph = pkv.paged_attention_workgroups_per_head(n, c.num_kv_heads, c.head_dim, c.block_size, 200 * c.block_size)
     say(f"  {n} sequences, {wph} workgroups per kv head: append {'folded' if n <= wph else 'launched first'}")
+
+
+@pytest.mark.parametrize("lens", [[17000], [17000, 40]], ids=["one-seq-folded", "two-seqs-launched"])
+def test_segment_longer_than_one_id_chunk(lens):
+    """One workgroup per kv head (partition_size past the batch) walks a
+    segment of 1063 blocks, more than one chunk of staged block ids: the
+    appended row lands in the last chunk, after the first chunk's barrier.
+    One sequence folds the append (1 <= 1 workgroup per head), two launch it
+    first."""
+    import paged_kv_cache_230_amd as pkv
+
+    say(f"case decode_append long segment {lens}")
+    bs, d, Hq, Hkv = 16, 128, 8, 2
+    g = torch.Generator().manual_seed(1063)
+    S = len(lens)
+    nb = sum(-(-L // bs) for L in lens) + 3
+    perm = torch.randperm(nb, generator=g).numpy()
+    maxb = max(-(-L // bs) for L in lens)
+    tables = np.full((S, maxb), -1, np.int32)
+    used = 0
+    for s, L in enumerate(lens):
+        n = -(-L // bs)
+        tables[s, :n] = perm[used:used + n]
+        used += n
+    hist = [(s, t) for s, L in enumerate(lens) for t in range(L - 1)]
+    slots = np.array([int(tables[s, t // bs]) * bs + t % bs for s, t in hist], np.int64)
+    std = 128 ** -0.5
+    kh = (torch.randn(len(hist), Hkv, d, generator=g) * std).to(torch.bfloat16)
+    vh = (torch.randn(len(hist), Hkv, d, generator=g) * std).to(torch.bfloat16)
+    kn = (torch.randn(S, Hkv, d, generator=g) * std).to(torch.bfloat16)
+    vn = (torch.randn(S, Hkv, d, generator=g) * std).to(torch.bfloat16)
+    q = (torch.randn(S, Hq, d, generator=g) * std * 64).to(torch.bfloat16)
+    part = S * max(lens)  # one workgroup per kv head
+    assert pkv.paged_attention_workgroups_per_head(S, Hkv, d, bs, max(lens), part) == 1
+    kA, vA = pkv.new_pools(nb, Hkv, d, bs, torch.bfloat16)
+    kA.fill_(float("nan"))
+    vA.fill_(float("nan"))
+    pkv.paged_kv_append(kh.cuda(), vh.cuda(), kA, vA, torch.from_numpy(slots.astype(np.int32)).cuda())
+    kB, vB = kA.clone(), vA.clone()
+    tab = torch.from_numpy(tables).cuda()
+    ln = torch.tensor(lens, dtype=torch.int32).cuda()
+    new_slots = torch.tensor([int(tables[s, (L - 1) // bs]) * bs + (L - 1) % bs for s, L in enumerate(lens)],
+                             dtype=torch.int32).cuda()
+    outA = torch.empty(S, Hq, d, dtype=torch.bfloat16, device="cuda")
+    pkv.paged_kv_append(kn.cuda(), vn.cuda(), kA, vA, new_slots)
+    pkv.paged_attention_decode(outA, q.cuda(), kA, vA, tab, ln, max(lens), partition_size=part)
+    outB = torch.empty_like(outA)
+    pkv.paged_attention_decode_append(outB, q.cuda(), kn.cuda(), vn.cuda(), kB, vB, tab, ln, max(lens),
+                                      partition_size=part)
+    torch.cuda.synchronize()
+    assert _bits_equal(kA, kB) and _bits_equal(vA, vB), "pools differ from append + decode"
+    assert _bits_equal(outA, outB), "outputs differ from append + decode"
+    ok, ov = opool.new_pools(nb, Hkv, d, bs, np.uint16)
+
+    def st(t):
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    opool.append(ok, ov, np.concatenate([st(kh), st(kn)]), np.concatenate([st(vh), st(vn)]),
+                 np.concatenate([slots, new_slots.cpu().numpy().astype(np.int64)]))
+    ref = oatt.decode_attention(st(q), ok, ov, tables, np.array(lens))
+    assert_close(outB, ref, "bf16", f"decode_append long segment {lens}")
