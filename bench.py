@@ -898,6 +898,9 @@ def main():
         "decode_calls_marked": len(dec_ms),
         "decode_tflops": round((sum(flops) / len(flops)) / mean_dec_s / 1e12, 2),
         "cow_pairs": n_cow_total,
+        # the single call writes the step's rows from inside the decode kernel
+        # when there is at most one sequence per decode workgroup of a kv head
+        "append_folded": (not args.separate_append) and S <= wph,
         "host_us_per_step": round(1e6 * sum(host_s[k] for k in timed) / args.steps, 1),
         "roofline": {
             "bound": "hbm",
