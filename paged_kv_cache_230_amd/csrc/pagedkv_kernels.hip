@@ -31,6 +31,11 @@
 //   * The 4 waves merge in LDS; a sequence that fits one partition writes
 //     the output, otherwise the partition writes (max, sum, unnormalised
 //     accumulator) partials and a merge kernel combines them.
+//   * A decode step's one-token cache append (step 3 of the aitalk page)
+//     can ride along: the workgroup that reads a sequence's last block
+//     first writes the new K/V row into it.  This is done only while each
+//     workgroup has at most one such row; otherwise a small append kernel
+//     runs first.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
