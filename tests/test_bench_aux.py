@@ -19,6 +19,13 @@ def test_decode_bytes_70b_32k_closed_form():
     assert bench.decode_algorithmic_bytes(lens, 64, 8, 128, 16, 2) == kv + qo + tables + 4 * 16 == 2148466816
 
 
+def test_append_bytes_count_one_row_per_nonempty_sequence():
+    # each non-empty sequence's new K and V rows: read once from k_new/v_new, written once into the pool
+    assert bench.append_algorithmic_bytes([32773] * 16, 8, 128, 2) == 16 * 8 * 128 * 2 * 2 * 2 == 65536
+    assert bench.append_algorithmic_bytes([5, 0, 1], 2, 64, 4) == 2 * (2 * 64 * 4) * 2 * 2
+    assert bench.append_algorithmic_bytes([], 8, 128, 2) == 0
+
+
 def test_prefill_flops_equal_brute_force():
     lens, chunks = [7, 20, 5], [3, 20, 1]
     brute = 0
