@@ -21,7 +21,8 @@ def test_decode_bytes_70b_32k_closed_form():
 
 def test_append_bytes_count_one_row_per_nonempty_sequence():
     # each non-empty sequence's new K and V rows: read once from k_new/v_new, written once into the pool
-    assert bench.append_algorithmic_bytes([32773] * 16, 8, 128, 2) == 16 * 8 * 128 * 2 * 2 * 2 == 65536
+    # 70B step: 16 x 8 x 128 bf16 = 32 KiB of K rows and 32 KiB of V rows, each read and written: 128 KiB
+    assert bench.append_algorithmic_bytes([32773] * 16, 8, 128, 2) == 16 * 8 * 128 * 2 * 2 * 2 == 131072
     assert bench.append_algorithmic_bytes([5, 0, 1], 2, 64, 4) == 2 * (2 * 64 * 4) * 2 * 2
     assert bench.append_algorithmic_bytes([], 8, 128, 2) == 0
 
