@@ -160,9 +160,11 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         raise ValueError("block_tables/context_lens must have num_seqs rows")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = paged_attention_workspace_bytes(S, Hq, H, d, bs, int(max_context_len), partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        # the library checks a caller's workspace against the size it needs
+        need = paged_attention_workspace_bytes(S, Hq, H, d, bs, int(max_context_len), partition_size)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, dev, 1)
     N.check(
@@ -197,9 +199,11 @@ def paged_attention_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_
         raise ValueError("block_tables/context_lens must have num_seqs rows")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = paged_attention_workspace_bytes(S, Hq, H, d, bs, int(max_context_len), partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        # the library checks a caller's workspace against the size it needs
+        need = paged_attention_workspace_bytes(S, Hq, H, d, bs, int(max_context_len), partition_size)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, dev, 1)
     N.check(
