@@ -278,8 +278,8 @@ def test_small_workspace_is_rejected_before_any_launch():
     q = torch.ones(S, Hq, d, dtype=torch.bfloat16, device="cuda")
     kn = torch.full((S, Hkv, d), 2.0, dtype=torch.bfloat16, device="cuda")
     out = torch.empty_like(q)
-    need = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, d, bs, max(lens))
-    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    # 512 bytes: below the piece records and partial maxima alone, at any occupancy
+    small = torch.empty(512, dtype=torch.uint8, device="cuda")
     with pytest.raises(PKVError, match="workspace"):
         pkv.paged_attention_decode(out, q, k, v, tables, ln, max(lens), workspace=small)
     with pytest.raises(PKVError, match="workspace"):
