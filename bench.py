@@ -131,6 +131,37 @@ def calibration_copy(dev):
     del src, dst
 
 
+def measured_read_peak(dev, nbytes=4 << 30, reps=6):
+    """HBM read rate of the library's plain streaming probe (pkv_stream_read)
+    over a buffer larger than every cache, timed with HIP events on the
+    current stream: (best, median) in bytes/s over ``reps`` reads after one
+    untimed read."""
+    import torch
+
+    import paged_kv_cache_230_amd as pkv
+
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(2048 * 4, dtype=torch.int32, device=dev)
+    pkv.stream_read(buf, sink)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for r in range(reps):
+        pkv.stream_read(buf, sink)
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    rates = sorted(nbytes / (ev[r].elapsed_time(ev[r + 1]) / 1e3) for r in range(reps))
+    del buf, sink
+    torch.cuda.empty_cache()
+    return rates[-1], rates[len(rates) // 2]
+
+
+def percentiles(xs, ps=(10, 50, 90)):
+    """Nearest-rank percentiles of a list."""
+    ys = sorted(xs)
+    return {f"p{p}": ys[min(len(ys) - 1, max(0, math.ceil(p / 100 * len(ys)) - 1))] for p in ps}
+
+
 def prefix_cache_report(w):
     """Host cost and effect of the prefix cache on a workload of cached
     admissions: the admissions replayed on a fresh block manager (host only,
@@ -699,6 +730,8 @@ def main():
                     help="append with paged_kv_append, then paged_attention_decode (two calls) instead of "
                          "paged_attention_decode_append")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences in the oracle sample (default: all)")
+    ap.add_argument("--marked", type=int, default=50,
+                    help="event-timed decode calls for the roofline, and event-bounded steps for the distribution")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter calibration)")
     ap.add_argument("--aux-paging", action="store_true",
@@ -746,9 +779,11 @@ def main():
     S = w.num_seqs
     # Warm-up steps, the timed steps (no markers between kernels: each event
     # marker costs a dispatch gap), then a pass of marked steps whose HIP
-    # events time each decode call for the roofline figure.
-    n_marked = min(args.steps, 10)
-    nsteps = args.warmup + args.steps + n_marked
+    # events time each decode call for the roofline figure, then a pass with
+    # one event at each step boundary for the distribution of step times.
+    n_marked = args.marked
+    n_dist = args.marked
+    nsteps = args.warmup + args.steps + n_marked + n_dist + 1
     print(f"# setup {w.name}: {S} sequences, pool {w.num_blocks} blocks", file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
     cache = pkv.PagedKVCache(w.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.torch_dtype, dev,
@@ -787,7 +822,8 @@ def main():
     stage = [torch.zeros(stage_cap, dtype=torch.int32, pin_memory=True) for _ in range(nsteps)]
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
     ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps)]
-    marked = range(args.warmup + args.steps, nsteps)
+    marked = range(args.warmup + args.steps, args.warmup + args.steps + n_marked)
+    dist = range(args.warmup + args.steps + n_marked, nsteps)  # an event after each of these steps
     host_s = [0.0] * nsteps
     seg = {"wait": 0.0, "bookkeeping+stage": 0.0, "copy+append": 0.0, "decode": 0.0}
     step_lens = []
@@ -814,7 +850,7 @@ def main():
         else:
             pkv.paged_attention_decode_append(out, step_q[k], step_k[k], step_v[k], cache.k_cache, cache.v_cache,
                                               tables_d, lens_d, max_len, partition_size=P, workspace=workspace)
-        if k in marked:
+        if k in marked or k in dist:
             ev1[k].record()
         t4 = time.perf_counter()
         host_s[k] = t4 - th
@@ -836,6 +872,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     for k in marked:
+        step(k)
+    for k in dist:
         step(k)
     torch.cuda.synchronize()
     print(f"# timed {args.steps} steps in {elapsed:.4f}s; host us/step by segment: "
@@ -862,6 +900,13 @@ def main():
     flops = [decode_flops(L, c.num_q_heads, c.head_dim) for L in lens_m]
     mean_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
     achieved = (sum(alg_bytes) / len(alg_bytes)) / mean_dec_s
+    # step times between consecutive boundary events (one marker per step)
+    dk = list(dist)
+    step_us = [1e3 * ev1[dk[i - 1]].elapsed_time(ev1[dk[i]]) for i in range(1, len(dk))]
+    step_kv = [decode_kv_bytes(step_lens[dk[i]], c.num_kv_heads, c.head_dim, c.elem_bytes) for i in range(1, len(dk))]
+    step_gbps = [b / (t * 1e-6) / 1e9 for b, t in zip(step_kv, step_us)]
+    dec_us = [1e3 * t for t in dec_ms]
+    peak_read, median_read = measured_read_peak(dev)
     ms_per_step = elapsed / args.steps * 1e3
     value = sum(kv_bytes) / elapsed / 1e9
     traffic = load_traffic(w.name, P) if not args.separate_append else None
@@ -914,6 +959,17 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_call": int(sum(alg_bytes) / len(alg_bytes)),
             "unique_kv_block_bytes_last_call": unique_blocks * block_bytes,
+            "calls_timed": len(dec_ms),
+            "call_us": {k: round(v, 2) for k, v in percentiles(dec_us).items()},
+            "measured_read_peak_gbps": round(peak_read / 1e9, 1),
+            "measured_read_median_gbps": round(median_read / 1e9, 1),
+            "frac_of_measured_peak": round(achieved / peak_read, 4),
+        },
+        "step_distribution": {
+            "steps": len(step_us),
+            "note": "one HIP event at each step boundary (a marker adds a dispatch gap to every step)",
+            "step_us": {k: round(v, 2) for k, v in percentiles(step_us).items()},
+            "kv_gbps": {k: round(v, 1) for k, v in percentiles(step_gbps).items()},
         },
         "cpu_baseline": None,
     }

@@ -74,12 +74,44 @@ extern "C" {
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 
+/* Flags of the device status word (pkv_device_status).  A kernel that
+ * meets a device-side index outside its range skips (or, for decode
+ * reads, clamps into the buffers) the access it names and ORs one of these
+ * into the word of the GPU it runs on; results that depend on the value
+ * are then unspecified, but no access leaves the buffers. */
+#define PKV_DEV_BAD_BLOCK_ID 1    /* a block-table entry in use outside [0, num_blocks) */
+#define PKV_DEV_BAD_LENGTH 2      /* a context length outside [0, max_context_len]     */
+#define PKV_DEV_BAD_SLOT 4        /* an append slot at or past num_blocks * block_size  */
+#define PKV_DEV_BAD_PAIR 8        /* a copy or swap pair naming a block outside a pool  */
+#define PKV_DEV_BAD_RECORD 16     /* a staged table update outside the device table     */
+#define PKV_DEV_BAD_QUERY_START 32 /* prefill query_start not rising in [0, num_tokens] */
+
 /* Message for the last failing call on this thread ("" if none).  The
  * string is owned by the library and valid until the thread's next call. */
 const char* pkv_last_error(void);
 
+/* Measurement helper: reads `bytes` (a multiple of 16) of device memory at
+ * `buf` (16-byte aligned) once with a plain streaming kernel of
+ * min(bytes / 4096, sink_words) workgroups, each folding what it read into
+ * one word of `sink` (device uint32 [sink_words]).  Timing it gives the
+ * HBM read rate this GPU reaches for a simple stream, the practical ceiling
+ * beside the nominal peak for the bandwidth-bound decode kernel ([pl]
+ * Złożoność obliczeniowa: the kernel is bound by HBM bandwidth).
+ * Asynchronous on `stream`. */
+int32_t pkv_stream_read(const void* buf, size_t bytes, void* sink, int32_t sink_words, void* stream);
+
 /* Library interface version (major * 100 + minor). */
 int32_t pkv_version(void);
+
+/* Device status word of the current GPU: waits for `stream`, stores the
+ * OR of the PKV_DEV_* flags that kernels have set since the word was last
+ * cleared in *flags_out (0 = every device-side index was in range), and
+ * clears the word when `clear` is nonzero.  The word is shared by every
+ * call on that GPU; work running on other streams meanwhile may set a flag
+ * between the read and the clear.  Not for use under graph capture (it
+ * synchronises).  Errors: PKV_ERR_INVALID_ARG (null flags_out),
+ * PKV_ERR_DEVICE (no device, a failed copy). */
+int32_t pkv_device_status(void* stream, int32_t clear, int32_t* flags_out);
 
 /* ------------------------------------------------------------------ */
 /* Cache append ([aitalk] step 3: the cache grows one slot at a time; a  */
@@ -89,7 +121,9 @@ int32_t pkv_version(void);
 /*                16-byte aligned rows                                    */
 /* k_cache, v_cache : device pools in the format above, num_blocks blocks */
 /* slot_mapping : device int32 [num_tokens]; slot < 0 skips the token;    */
-/*                slots must be distinct (duplicates race)                */
+/*                slots must be distinct (duplicates race); a slot at or  */
+/*                past num_blocks * block_size is skipped and sets        */
+/*                PKV_DEV_BAD_SLOT                                        */
 /* Writes K/V of each token into its slot; every other byte is untouched. */
 /* num_tokens == 0 is a no-op.                                            */
 int32_t paged_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -141,7 +175,11 @@ int32_t paged_kv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, 
 /* k_cache, v_cache : device pools, num_blocks blocks                     */
 /* block_tables  : device int32 [num_seqs][max_blocks_per_seq]; entries   */
 /*                 past ceil(L / block_size) are not read                 */
-/* context_lens  : device int32 [num_seqs], each in [0, max_context_len]  */
+/* context_lens  : device int32 [num_seqs], each in [0, max_context_len]; */
+/*                 a value outside is clamped into that range and sets    */
+/*                 PKV_DEV_BAD_LENGTH; a table entry in use outside       */
+/*                 [0, num_blocks) reads block 0 and sets                 */
+/*                 PKV_DEV_BAD_BLOCK_ID                                   */
 /* max_context_len : host upper bound on context_lens, <=                 */
 /*                 max_blocks_per_seq * block_size                        */
 /* scale         : logit scale (usually 1/sqrt(head_dim))                 */
@@ -179,8 +217,11 @@ int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, co
 /* table).  For each sequence s with L = context_lens[s] > 0, the K/V    */
 /* rows of the token at position L - 1 are first written from            */
 /* k_new[s] / v_new[s] into slot (L-1) % block_size of block              */
-/* block_tables[s][(L-1) / block_size] (skipped if that id is outside    */
-/* [0, num_blocks)), then out is computed exactly as by                  */
+/* block_tables[s][(L-1) / block_size] (skipped, and PKV_DEV_BAD_BLOCK_ID */
+/* set, if that id is outside [0, num_blocks); a length outside          */
+/* [0, max_context_len] writes nothing and sets PKV_DEV_BAD_LENGTH, so a */
+/* max_context_len below the true lengths never overwrites a cached      */
+/* token), then out is computed exactly as by                            */
 /* paged_attention_decode.  Pools and out afterwards equal those of      */
 /* paged_kv_append with that slot mapping followed by                    */
 /* paged_attention_decode, bit for bit.  When num_seqs is at most the    */

@@ -10,6 +10,8 @@ from .api import (  # noqa: F401
     BlockManager,
     RadixIndex,
     block_digest,
+    device_status,
+    stream_read,
     host_pools,
     new_pools,
     paged_attention_decode,

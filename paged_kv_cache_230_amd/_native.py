@@ -28,6 +28,14 @@ PKV_ERR_CAPACITY = -6
 PKV_F32 = 0
 PKV_BF16 = 1
 
+# Flags of the device status word (pkv_device_status).
+PKV_DEV_BAD_BLOCK_ID = 1
+PKV_DEV_BAD_LENGTH = 2
+PKV_DEV_BAD_SLOT = 4
+PKV_DEV_BAD_PAIR = 8
+PKV_DEV_BAD_RECORD = 16
+PKV_DEV_BAD_QUERY_START = 32
+
 STATUS_NAMES = {
     PKV_ERR_INVALID_ARG: "INVALID_ARG",
     PKV_ERR_OUT_OF_BLOCKS: "OUT_OF_BLOCKS",
@@ -61,6 +69,8 @@ _pu8 = C.POINTER(C.c_uint8)
 _SIGS = {
     "pkv_last_error": (C.c_char_p, []),
     "pkv_version": (_i32, []),
+    "pkv_device_status": (_i32, [_vp, _i32, _pi32]),
+    "pkv_stream_read": (_i32, [_vp, _sz, _vp, _i32, _vp]),
     "paged_kv_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "paged_kv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "paged_attention_decode": (

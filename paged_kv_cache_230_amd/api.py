@@ -29,6 +29,8 @@ __all__ = [
     "paged_attention_workspace_bytes",
     "paged_attention_workgroups_per_head",
     "BlockManager",
+    "device_status",
+    "stream_read",
 ]
 
 _DT = {torch.float32: N.PKV_F32, torch.bfloat16: N.PKV_BF16}
@@ -59,6 +61,30 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None, ndim=None):
         raise ValueError(f"{name} must be on {device}, got {t.device}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def device_status(device=None, clear: bool = True) -> int:
+    """OR of the PKV_DEV_* flags kernels set on ``device`` since the last
+    clear (0: every device-side index was in range); waits for the current
+    stream first, and clears the word unless ``clear`` is false."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    flags = C.c_int32(0)
+    with torch.cuda.device(dev):
+        N.check(N.lib.pkv_device_status(_stream(dev), 1 if clear else 0, C.byref(flags)))
+    return int(flags.value)
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor):
+    """Read the whole of ``buf`` (a contiguous device tensor, 16-byte aligned,
+    a multiple of 16 bytes) once with the library's streaming probe on the
+    current stream; ``sink`` (device int32) receives one word per
+    workgroup."""
+    dev = buf.device
+    _need(sink, "sink", torch.int32, dev, 1)
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    N.check(N.lib.pkv_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), sink.numel(),
+                                  _stream(dev)))
 
 
 def pool_shapes(num_blocks, num_kv_heads, head_dim, block_size, dtype):

@@ -13,8 +13,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libpagedkv.so"
-SOURCES = ["csrc/pagedkv_kernels.hip", "csrc/prefill_kernel.hip", "csrc/swap_kernel.hip", "csrc/block_manager.cpp",
-           "csrc/radix.cpp"]
+SOURCES = ["csrc/pagedkv_kernels.hip", "csrc/prefill_kernel.hip", "csrc/swap_kernel.hip", "csrc/measure_kernel.hip",
+           "csrc/block_manager.cpp", "csrc/radix.cpp"]
 ARCH = "gfx950"
 
 

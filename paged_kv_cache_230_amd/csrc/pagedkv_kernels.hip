@@ -33,9 +33,10 @@
 //     accumulator) partials and a merge kernel combines them.
 //   * A decode step's one-token cache append (step 3 of the aitalk page)
 //     can ride along: the workgroup that reads a sequence's last block
-//     first writes the new K/V row into it.  This is done only while each
-//     workgroup has at most one such row; otherwise a small append kernel
-//     runs first.
+//     first writes the new K/V row into it (a workgroup whose range holds
+//     the ends of several short sequences writes one row per segment).
+//     This is done only when there are at most as many sequences as
+//     workgroups per kv head; otherwise a small append kernel runs first.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -76,6 +77,13 @@ __device__ __forceinline__ float row_rotate8(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
 }
 
+// Device status word (one per GPU): kernels OR a PKV_DEV_* flag into it when
+// they meet a device-side index outside its range (the offending access is
+// skipped or clamped into the buffers).  pkv_device_status reads and clears it.
+__device__ __forceinline__ void report(int32_t* status, int32_t flag) {
+  __hip_atomic_fetch_or(status, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -89,6 +97,7 @@ struct DecodeArgs {
   float* ws_m;       // [N][2][G] partial max (log2 domain)
   float* ws_l;       // [N][2][G] partial sum
   int32_t* meta;     // [S][Hkv][2] first workgroup index and number of pieces of (s, g)
+  int32_t* status;   // device status word
   int32_t wgs_per_head;  // N / Hkv
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -276,7 +285,10 @@ template <bool BF16, int D, int BS>
 __device__ __forceinline__ void append_store(const DecodeArgs& a, const AppendRow<BF16, D>& r, int g, int L) {
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int X = 16 / EB;
-  if (static_cast<unsigned>(r.blk) >= static_cast<unsigned>(a.num_blocks)) return;
+  if (static_cast<unsigned>(r.blk) >= static_cast<unsigned>(a.num_blocks)) {
+    if (threadIdx.x == 0) report(a.status, PKV_DEV_BAD_BLOCK_ID);
+    return;
+  }
   const int o = (L - 1) % BS;
   const size_t tile = (static_cast<size_t>(r.blk) * a.num_kv_heads + g) * static_cast<size_t>(D) * BS;
   char* kc = const_cast<char*>(static_cast<const char*>(a.k_cache));
@@ -359,11 +371,29 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
   auto compute_step = [&](Step<BF16, D>& st, const int tok_base) {
 
       // Scores S[token 4*quad+i][head row] for the 16 tokens of this step.
+      // bf16: the dot product runs as two chained halves (dims 0..D/2-1
+      // and D/2..D-1), whose results are summed without rounding error into
+      // sc + sl (Knuth's two-sum), so the score carries only the halves' own
+      // roundings.  With logits in the hundreds, rounding every partial sum
+      // of one chained product to fp32 moves the softmax weights of
+      // near-tied keys enough to show in outputs near zero.
       float4v sc = {0.f, 0.f, 0.f, 0.f};
+      float4v sl = {0.f, 0.f, 0.f, 0.f};
       if constexpr (BF16) {
+        constexpr int KK = D / 32;
+        float4v half_sum[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
   #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st.k[kk]), qo.q[kk], sc, 0, 0, 0);
+        for (int kk = 0; kk < KK; ++kk)
+          half_sum[kk / (KK / 2)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, st.k[kk]), qo.q[kk], half_sum[kk / (KK / 2)], 0, 0, 0);
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a0 = half_sum[0][i], b0 = half_sum[1][i];
+          const float s0 = a0 + b0;
+          const float bv = s0 - a0;
+          sl[i] = (a0 - (s0 - bv)) + (b0 - bv);
+          sc[i] = s0;
+        }
       } else {
   #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
@@ -390,8 +420,18 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
       const float m_new = fmaxf(m_run, bmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       float pr[4];
+      if constexpr (BF16) {
+        // exponent (sc + sl) * scale - m with the large terms in one fused
+        // operation: only the small remainder is rounded
   #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
+        for (int i = 0; i < 4; ++i) {
+          const float e = fmaf(sc[i], a.scale_log2, -m_new) + sl[i] * a.scale_log2;
+          pr[i] = x[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(e);
+        }
+      } else {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
+      }
       l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
       if (__any(m_new > m_run)) {
         // Accumulator row r = 4*quad + v holds head (r mod 8) for bf16 (rows
@@ -446,7 +486,9 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
     const int cn = nblk - c0 < kIdChunk ? nblk - c0 : kIdChunk;
     for (int i = threadIdx.x; i < cn; i += kThreads) {
       const int b = tbl[c0 + i];
-      sm.ids[i] = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks) ? b : 0;
+      const bool ok = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks);
+      if (!ok) report(a.status, PKV_DEV_BAD_BLOCK_ID);
+      sm.ids[i] = ok ? b : 0;
     }
   };
   // The first chunk's ids are staged before the loop, so the append (its
@@ -588,7 +630,12 @@ __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel
   int T = 0;
   for (int base = 0; base < S; base += kThreads) {
     const int s = base + threadIdx.x;
-    const int nb = s < S ? (clamp_len(a.context_lens[s], a.max_context_len) + BS - 1) / BS : 0;
+    int nb = 0;
+    if (s < S) {
+      const int Lr = a.context_lens[s];
+      if ((Lr < 0 || Lr > a.max_context_len) && k == 0) report(a.status, PKV_DEV_BAD_LENGTH);
+      nb = (clamp_len(Lr, a.max_context_len) + BS - 1) / BS;
+    }
     int tot;
     block_scan<BF16, D>(nb, &tot, sm);
     T += tot;
@@ -624,14 +671,17 @@ __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel
 
   // Walk the segments of [b0, b1).
   for (; s < S && pre < b1; ++s) {
-    const int L = clamp_len(a.context_lens[s], a.max_context_len);
+    const int Lr = a.context_lens[s];
+    const int L = clamp_len(Lr, a.max_context_len);
     const int nb = (L + BS - 1) / BS;
     if (nb == 0) continue;
     const int lb0 = static_cast<int>((b0 > pre ? b0 : pre) - pre);
     const int lb1 = static_cast<int>((b1 < static_cast<int64_t>(pre) + nb ? b1 : static_cast<int64_t>(pre) + nb) - pre);
     const bool whole = lb0 == 0 && lb1 == nb;
     const int prow = whole ? -1 : (b * 2 + (lb0 == 0 ? 1 : 0));
-    decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, appending && lb1 == nb, sm);
+    // A length outside [1, max_context_len] appends nothing: a clamped length
+    // would name a slot that already holds a cached token.
+    decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, appending && lb1 == nb && Lr == L, sm);
     if (lb0 == 0 && threadIdx.x == 0) {
       // Workgroup (within this head) holding block x of the list: the largest
       // k' with k' T / Ng <= x.
@@ -769,7 +819,7 @@ __global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ k_
                                                      char* __restrict__ k_cache, char* __restrict__ v_cache,
                                                      const int32_t* __restrict__ slot_mapping, int64_t total,
                                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                                     int32_t num_blocks) {
+                                                     int32_t num_blocks, int32_t* __restrict__ status) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int nch = head_dim / (16 / EB);
@@ -778,15 +828,20 @@ __global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ k_
   const int h = static_cast<int>(th % num_kv_heads);
   const int64_t t = th / num_kv_heads;
   const int32_t slot = slot_mapping[t];
-  if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(num_blocks) * block_size) return;
+  if (slot < 0) return;
+  if (static_cast<int64_t>(slot) >= static_cast<int64_t>(num_blocks) * block_size) {
+    report(status, PKV_DEV_BAD_SLOT);
+    return;
+  }
   const int64_t row = t * num_kv_heads * head_dim * EB;
   write_row_chunk<EB>(k_new + row, v_new + row, k_cache, v_cache, slot, h, c, num_kv_heads, head_dim, block_size);
 }
 
 // The decode step's one-token append as its own launch: sequence s's row
-// goes to the slot of position L - 1 (L = its clamped context length),
-// found through its block table; L == 0 or a block id outside the pool
-// skips it.  One thread per (sequence, kv head, 16-byte chunk).
+// goes to the slot of position L - 1 (L = its context length), found
+// through its block table.  L == 0 skips it; a length outside
+// [0, max_context_len] or a block id outside the pool skips it and is
+// reported.  One thread per (sequence, kv head, 16-byte chunk).
 template <int EB>
 __global__ __launch_bounds__(256) void append_last_kernel(const char* __restrict__ k_new,
                                                           const char* __restrict__ v_new, char* __restrict__ k_cache,
@@ -795,7 +850,7 @@ __global__ __launch_bounds__(256) void append_last_kernel(const char* __restrict
                                                           const int32_t* __restrict__ context_lens, int64_t total,
                                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                                           int32_t num_blocks, int32_t max_blocks_per_seq,
-                                                          int32_t max_context_len) {
+                                                          int32_t max_context_len, int32_t* __restrict__ status) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int nch = head_dim / (16 / EB);
@@ -803,10 +858,17 @@ __global__ __launch_bounds__(256) void append_last_kernel(const char* __restrict
   const int64_t th = idx / nch;
   const int h = static_cast<int>(th % num_kv_heads);
   const int64_t s = th / num_kv_heads;
-  const int L = clamp_len(context_lens[s], max_context_len);
+  const int L = context_lens[s];
   if (L == 0) return;
+  if (L < 0 || L > max_context_len) {
+    if (c == 0 && h == 0) report(status, PKV_DEV_BAD_LENGTH);
+    return;
+  }
   const int32_t blk = block_tables[s * max_blocks_per_seq + (L - 1) / block_size];
-  if (blk < 0 || blk >= num_blocks) return;
+  if (blk < 0 || blk >= num_blocks) {
+    if (c == 0 && h == 0) report(status, PKV_DEV_BAD_BLOCK_ID);
+    return;
+  }
   const int64_t slot = static_cast<int64_t>(blk) * block_size + (L - 1) % block_size;
   const int64_t row = s * num_kv_heads * head_dim * EB;
   write_row_chunk<EB>(k_new + row, v_new + row, k_cache, v_cache, slot, h, c, num_kv_heads, head_dim, block_size);
@@ -815,11 +877,14 @@ __global__ __launch_bounds__(256) void append_last_kernel(const char* __restrict
 // Block copy: blockIdx.x = pair, blockIdx.y = 0 (K pool) or 1 (V pool).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
                                                           const int32_t* __restrict__ src_dst, int64_t block_bytes,
-                                                          int32_t num_blocks) {
+                                                          int32_t num_blocks, int32_t* __restrict__ status) {
   const int pair = blockIdx.x;
   const int32_t src = src_dst[2 * pair];
   const int32_t dst = src_dst[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) {
+    if (threadIdx.x == 0 && blockIdx.y == 0) report(status, PKV_DEV_BAD_PAIR);
+    return;
+  }
   char* pool = blockIdx.y == 0 ? k_cache : v_cache;
   const uint4* from = reinterpret_cast<const uint4*>(pool + static_cast<int64_t>(src) * block_bytes);
   uint4* to = reinterpret_cast<uint4*>(pool + static_cast<int64_t>(dst) * block_bytes);
@@ -833,7 +898,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_c
 __global__ __launch_bounds__(256) void stage_kernel(const int32_t* __restrict__ stage, int32_t n, int32_t np,
                                                    int32_t nu, int32_t width, int32_t* __restrict__ slots,
                                                    int32_t* __restrict__ lens, int32_t* __restrict__ pairs,
-                                                   int32_t* __restrict__ tables) {
+                                                   int32_t* __restrict__ tables, int32_t* __restrict__ status) {
   const int32_t* s_slots = stage + 4;
   const int32_t* s_lens = s_slots + n;
   const int32_t* s_pairs = s_lens + n;
@@ -851,7 +916,10 @@ __global__ __launch_bounds__(256) void stage_kernel(const int32_t* __restrict__ 
       const int64_t u = i - 2LL * n - 2LL * np;
       const int32_t row = s_upd[3 * u];
       const int32_t col = s_upd[3 * u + 1];
-      if (row >= 0 && row < n && col >= 0 && col < width) tables[static_cast<int64_t>(row) * width + col] = s_upd[3 * u + 2];
+      if (row >= 0 && row < n && col >= 0 && col < width)
+        tables[static_cast<int64_t>(row) * width + col] = s_upd[3 * u + 2];
+      else
+        report(status, PKV_DEV_BAD_RECORD);
     }
   }
 }
@@ -968,6 +1036,11 @@ void dispatch_bs(const DecodeArgs& a, int32_t bs, hipStream_t st) {
 
 }  // namespace
 
+// The device status word: every GPU the library runs on holds its own copy
+// (kernels reach it through the address pkv::device_status_ptr returns for
+// the current device).
+__device__ int32_t g_pkv_device_status;
+
 namespace pkv {
 std::string& last_error_slot() {
   thread_local std::string msg;
@@ -996,15 +1069,40 @@ int32_t stage_device_ptr(const int32_t* stage, const int32_t** dev_out) {
   return PKV_OK;
 }
 
+int32_t device_status_ptr(int32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int32_t*> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_DEVICE, "no usable current device for the status word");
+  }
+  int32_t* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* addr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(g_pkv_device_status));
+    if (e != hipSuccess || !addr) {
+      (void)hipGetLastError();
+      return fail(PKV_ERR_DEVICE, "status word address: %s", hipGetErrorString(e));
+    }
+    p = static_cast<int32_t*>(addr);
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PKV_OK;
+}
+
 int32_t launch_stage(const int32_t* stage_dev, int32_t n_seqs, int32_t n_pairs, int32_t n_updates, int32_t width,
                      int32_t* slot_mapping, int32_t* context_lens, int32_t* cow_pairs, int32_t* block_tables,
                      void* stream) {
+  int32_t* status = nullptr;
+  if (int32_t e = device_status_ptr(&status)) return e;
   const int64_t total = 2LL * n_seqs + 2LL * n_pairs + n_updates;
   int64_t grid = (total + 255) / 256;
   if (grid > 1024) grid = 1024;
   if (grid < 1) grid = 1;
   stage_kernel<<<dim3(static_cast<uint32_t>(grid)), 256, 0, static_cast<hipStream_t>(stream)>>>(
-      stage_dev, n_seqs, n_pairs, n_updates, width, slot_mapping, context_lens, cow_pairs, block_tables);
+      stage_dev, n_seqs, n_pairs, n_updates, width, slot_mapping, context_lens, cow_pairs, block_tables, status);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_DEVICE, "stage launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
@@ -1015,7 +1113,26 @@ extern "C" {
 
 const char* pkv_last_error(void) { return pkv::last_error_slot().c_str(); }
 
-int32_t pkv_version(void) { return 100; }
+int32_t pkv_version(void) { return 101; }
+
+int32_t pkv_device_status(void* stream, int32_t clear, int32_t* flags_out) {
+  if (!flags_out) return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  int32_t* status = nullptr;
+  if (int32_t e = pkv::device_status_ptr(&status)) return e;
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  int32_t v = 0;
+  if (e == hipSuccess) e = hipMemcpy(&v, status, sizeof(v), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear) {
+    const int32_t zero = 0;
+    e = hipMemcpy(status, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return pkv::fail(PKV_ERR_DEVICE, "reading the device status word: %s", hipGetErrorString(e));
+  }
+  *flags_out = v;
+  return pkv::ok();
+}
 
 int32_t paged_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                         const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
@@ -1033,15 +1150,17 @@ int32_t paged_kv_append(const void* k_new, const void* v_new, void* k_cache, voi
   const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim * eb / 16);
   const int64_t blocks = (total + 255) / 256;
   if (blocks > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "too many tokens for one launch");
+  int32_t* status = nullptr;
+  if (int32_t e = pkv::device_status_ptr(&status)) return e;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (eb == 2)
     append_kernel<2><<<dim3(static_cast<uint32_t>(blocks)), 256, 0, st>>>(
         static_cast<const char*>(k_new), static_cast<const char*>(v_new), static_cast<char*>(k_cache),
-        static_cast<char*>(v_cache), slot_mapping, total, num_kv_heads, head_dim, block_size, num_blocks);
+        static_cast<char*>(v_cache), slot_mapping, total, num_kv_heads, head_dim, block_size, num_blocks, status);
   else
     append_kernel<4><<<dim3(static_cast<uint32_t>(blocks)), 256, 0, st>>>(
         static_cast<const char*>(k_new), static_cast<const char*>(v_new), static_cast<char*>(k_cache),
-        static_cast<char*>(v_cache), slot_mapping, total, num_kv_heads, head_dim, block_size, num_blocks);
+        static_cast<char*>(v_cache), slot_mapping, total, num_kv_heads, head_dim, block_size, num_blocks, status);
   return launch_status("paged_kv_append");
 }
 
@@ -1058,8 +1177,10 @@ int32_t paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ds
     return pkv::fail(PKV_ERR_INVALID_ARG, "K/V pools must be 16-byte aligned");
   const int eb = dt == PKV_BF16 ? 2 : 4;
   const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * eb;
+  int32_t* status = nullptr;
+  if (int32_t e = pkv::device_status_ptr(&status)) return e;
   copy_blocks_kernel<<<dim3(num_pairs, 2), 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<char*>(k_cache), static_cast<char*>(v_cache), src_dst, block_bytes, num_blocks);
+      static_cast<char*>(k_cache), static_cast<char*>(v_cache), src_dst, block_bytes, num_blocks, status);
   return launch_status("paged_kv_copy_blocks");
 }
 
@@ -1142,6 +1263,8 @@ int32_t decode_call(void* out, const void* q, const void* k_new, const void* v_n
     return pkv::fail(PKV_ERR_CAPACITY, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return pkv::fail(PKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  int32_t* status = nullptr;
+  if (int32_t e = pkv::device_status_ptr(&status)) return e;
   DecodeArgs a;
   a.out = out;
   a.q = q;
@@ -1149,13 +1272,15 @@ int32_t decode_call(void* out, const void* q, const void* k_new, const void* v_n
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  // The append is folded into the decode kernel only when there is at most
-  // one appended (sequence, kv head) row per decode workgroup.  Each row's
-  // V part is head_dim two-byte stores (the V tile is dimension-major);
-  // many of them issued into the decode kernel's saturated read stream cost
-  // more than a separate launch (measured: +27 us on 256 sequences x 8 kv
-  // heads over 768 workgroups, against -4 us of launch saved on 16 x 8).
-  // Both ways write the same bytes.
+  // The append is folded into the decode kernel only when there are at
+  // most as many sequences as decode workgroups per kv head, so there is on
+  // average at most one appended (sequence, kv head) row per workgroup (a
+  // workgroup whose range holds several short sequences still writes one row
+  // for each).  Each row's V part is head_dim two-byte stores (the V tile
+  // is dimension-major); many of them issued into the decode kernel's
+  // saturated read stream cost more than a separate launch (measured: +27 us
+  // on 256 sequences x 8 kv heads over 768 workgroups, against -4 us of
+  // launch saved on 16 x 8).  Both ways write the same bytes.
   const bool fold = k_new != nullptr && static_cast<int64_t>(num_seqs) <= wph;
   if (k_new != nullptr && !fold) {
     const int eb = dt == PKV_BF16 ? 2 : 4;
@@ -1167,13 +1292,13 @@ int32_t decode_call(void* out, const void* q, const void* k_new, const void* v_n
           static_cast<const char*>(k_new), static_cast<const char*>(v_new),
           const_cast<char*>(static_cast<const char*>(k_cache)), const_cast<char*>(static_cast<const char*>(v_cache)),
           block_tables, context_lens, total, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-          max_context_len);
+          max_context_len, status);
     else
       append_last_kernel<4><<<dim3(static_cast<uint32_t>(blocks)), 256, 0, ast>>>(
           static_cast<const char*>(k_new), static_cast<const char*>(v_new),
           const_cast<char*>(static_cast<const char*>(k_cache)), const_cast<char*>(static_cast<const char*>(v_cache)),
           block_tables, context_lens, total, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-          max_context_len);
+          max_context_len, status);
   }
   a.k_new = fold ? k_new : nullptr;
   a.v_new = fold ? v_new : nullptr;
@@ -1182,6 +1307,7 @@ int32_t decode_call(void* out, const void* q, const void* k_new, const void* v_n
   a.ws_m = reinterpret_cast<float*>(ws + wl.m);
   a.ws_l = reinterpret_cast<float*>(ws + wl.l);
   a.ws_acc = reinterpret_cast<float*>(ws + wl.acc);
+  a.status = status;
   a.wgs_per_head = static_cast<int32_t>(wph);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;

@@ -26,6 +26,10 @@ inline int32_t fail(int32_t code, const char* fmt, ...) {
 // Device address of a pinned host buffer (error if it is not pinned).
 int32_t stage_device_ptr(const int32_t* stage, const int32_t** dev);
 
+// Device address of the current GPU's status word (kernels OR PKV_DEV_*
+// flags into it); an error status if the device or the symbol is unusable.
+int32_t device_status_ptr(int32_t** out);
+
 // Launches the staging kernel that copies one decode step's record from
 // pinned host memory (read in place by the GPU, at `stage_dev`) into the
 // device buffers.

@@ -28,6 +28,9 @@
 //     holds 16 scores of row l%32, keys 16(j/8)+8(l/32)+j%8, so a row's max
 //     needs one partner lane, and those scores in that order are the B
 //     operand of the PV product: O^T += V^T P^T, again 32x32x16.
+//   * The probabilities enter the value product as bf16 high and low parts
+//     (two products per tile), so they keep about 2^-17 relative precision;
+//     the scores are two chained half dot products summed at the end.
 //   * Online softmax per row in the log2 domain; row maxima by the gfx950
 //     row swap v_permlane32_swap, not LDS shuffles; the causal mask (a
 //     select, never a multiply) only on the steps that reach past the tile's
@@ -74,7 +77,13 @@ struct PrefillArgs {
   int32_t num_seqs;
   int32_t ntiles;  // query tiles of the longest chunk
   float scale_log2;
+  int32_t* status;  // device status word
 };
+
+// Sets a PKV_DEV_* flag in the device status word.
+__device__ __forceinline__ void report(int32_t* status, int32_t flag) {
+  __hip_atomic_fetch_or(status, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its
 // own L2.  Workgroup b runs on XCD b % 8; the mapping below gives every
@@ -234,13 +243,20 @@ struct StagePlan {
 };
 
 // Staged block ids [chunk_base, chunk_base + kIdChunk) of the sequence,
-// clamped to the pool.  Past the context the id is 0: such a block is read
-// but never used (its keys are masked and its V slots zeroed in LDS).
+// clamped to the pool (an id outside it is reported).  Past the context the
+// id is 0: such a block is read but never used (its keys are masked and its
+// V slots zeroed in LDS).
 __device__ __forceinline__ void fill_ids(const PrefillArgs& a, const int32_t* table, int chunk_base, int nblk,
                                          int32_t* ids) {
   for (int i = threadIdx.x; i < kIdChunk; i += kPThreads) {
     const int lb = chunk_base + i;
-    ids[i] = lb < nblk ? clampi(table[lb], 0, a.num_blocks - 1) : 0;
+    int id = 0;
+    if (lb < nblk) {
+      const int raw = table[lb];
+      id = clampi(raw, 0, a.num_blocks - 1);
+      if (id != raw) report(a.status, PKV_DEV_BAD_BLOCK_ID);
+    }
+    ids[i] = id;
   }
 }
 
@@ -307,12 +323,18 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  const int L = clampi(a.context_lens[s], 0, a.max_blocks_per_seq * BS);
+  const int Lraw = a.context_lens[s];
+  const int L = clampi(Lraw, 0, a.max_blocks_per_seq * BS);
   int q0 = a.query_start[s];
-  int C = a.query_start[s + 1] - q0;
+  const int Craw = a.query_start[s + 1] - q0;
+  int C = Craw;
   if (q0 < 0 || q0 > a.num_tokens) C = 0;
   C = clampi(C, 0, L < a.max_query_len ? L : a.max_query_len);
   if (q0 + C > a.num_tokens) C = a.num_tokens - q0;
+  if (slot % a.ntiles == 0 && threadIdx.x == 0) {  // one workgroup per (sequence, kv head) reports
+    if (Lraw != L) report(a.status, PKV_DEV_BAD_LENGTH);
+    if (C != Craw) report(a.status, PKV_DEV_BAD_QUERY_START);
+  }
   const int TQ = a.tokens_per_tile;
   const int ntiles = (C + TQ - 1) / TQ;
   const int tile = a.ntiles - 1 - slot % a.ntiles;  // latest tiles first
@@ -389,14 +411,21 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   const int key_col = lane & 31;  // QK A operand slot of this lane
   const int k_tile = key_col / BS, k_in = key_col % BS;
   const int k_off = k_tile * kTileBytes + (half * BS + k_in) * 16;
+  // The dot product runs as two chained halves (dims 0..D/2-1 and
+  // D/2..D-1) summed at the end: with logits in the hundreds, rounding every
+  // partial sum of one long chain to fp32 moves the softmax weights of
+  // near-tied keys enough to show in outputs near zero.
   auto qk = [&](const char* kl) {
-    float16v r = float16v{};
+    float16v r0 = float16v{}, r1 = float16v{};
 #pragma unroll
     for (int c = 0; c < kQChunks; ++c) {
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + k_off + c * 2 * BS * 16);
-      r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[c], r, 0, 0, 0);
+      if (c < kQChunks / 2)
+        r0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[c], r0, 0, 0, 0);
+      else
+        r1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[c], r1, 0, 0, 0);
     }
-    return r;
+    return r0 + r1;
   };
   // V operand offsets: PV product m, dim tile t; lane dim 32t + l%32 reads
   // keys 16m + 8(l/32) .. +7, i.e. chunk (16m + 8 half) / 8 of its row.
@@ -453,28 +482,38 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     // contents are unused: in bounds, result dropped).
     sn = qk(reinterpret_cast<const char*>(sm.stage[nx1]));
 
-    __bf16 pe[16];
+    // Each probability enters the value product as a bf16 high part and
+    // the bf16 rounding of the remainder, so it is carried to about 2^-17
+    // relative precision (one bf16 alone, 2^-9, leaves outputs near zero
+    // with relative errors of tens of percent).
+    __bf16 pe[16], pr[16];
     float sum;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float p = __builtin_amdgcn_exp2f(fmaf(x[j], a.scale_log2, -m_use));
       sum = j ? sum + p : p;
       pe[j] = static_cast<__bf16>(p);
+      pr[j] = static_cast<__bf16>(p - static_cast<float>(pe[j]));
     }
     l_run = l_run * alpha + sum;
 
     // ---- O^T += V^T P^T, two products of 16 keys: product m takes this
     // lane's scores j = 8m..8m+7, keys 16m + 8*half + i, the B operand's k
     // order; the V operand of lane l holds the same keys of dim 32t + l%32.
+    // The high and low parts of P each take one product with the same V
+    // operand.
     const char* sl = reinterpret_cast<const char*>(sm.stage[cur]);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const bf16x8 pb = bf16x8{pe[8 * m], pe[8 * m + 1], pe[8 * m + 2], pe[8 * m + 3],
                                pe[8 * m + 4], pe[8 * m + 5], pe[8 * m + 6], pe[8 * m + 7]};
+      const bf16x8 pbl = bf16x8{pr[8 * m], pr[8 * m + 1], pr[8 * m + 2], pr[8 * m + 3],
+                                pr[8 * m + 4], pr[8 * m + 5], pr[8 * m + 6], pr[8 * m + 7]};
 #pragma unroll
       for (int t = 0; t < kDimTiles; ++t) {
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(sl + v_off[m] + t * 32 * (BS / 8) * 16);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbl, acc[t], 0, 0, 0);
       }
     }
 
@@ -592,6 +631,7 @@ int32_t paged_attention_prefill(void* out, const void* q, const void* k_cache, c
   a.num_seqs = num_seqs;
   a.ntiles = static_cast<int32_t>(ntiles);
   a.scale_log2 = scale * 1.4426950408889634f;
+  if (int32_t e = pkv::device_status_ptr(&a.status)) return e;
   const dim3 grid(static_cast<uint32_t>(nblocks));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (head_dim == 128)

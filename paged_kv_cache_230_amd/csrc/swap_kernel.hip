@@ -33,16 +33,20 @@ int32_t launch_status(const char* what) {
 // Swap copy between two pools of the same format, either of which may be
 // pinned host memory read or written in place over the bus: blockIdx.x =
 // pair, blockIdx.y = 0 (K) or 1 (V).  Pairs naming blocks outside either
-// pool are skipped.
+// pool are skipped and set the bad-pair flag of the device status word.
 __global__ __launch_bounds__(256) void swap_blocks_kernel(const char* __restrict__ src_k,
                                                           const char* __restrict__ src_v, char* __restrict__ dst_k,
                                                           char* __restrict__ dst_v, const int32_t* __restrict__ pairs,
                                                           int64_t block_bytes, int32_t src_blocks,
-                                                          int32_t dst_blocks) {
+                                                          int32_t dst_blocks, int32_t* __restrict__ status) {
   const int pair = blockIdx.x;
   const int32_t s = pairs[2 * pair];
   const int32_t d = pairs[2 * pair + 1];
-  if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) return;
+  if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) {
+    if (threadIdx.x == 0 && blockIdx.y == 0)
+      __hip_atomic_fetch_or(status, PKV_DEV_BAD_PAIR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   const char* from = (blockIdx.y == 0 ? src_k : src_v) + static_cast<int64_t>(s) * block_bytes;
   char* to = (blockIdx.y == 0 ? dst_k : dst_v) + static_cast<int64_t>(d) * block_bytes;
   const int64_t n = block_bytes / 16;
@@ -97,8 +101,10 @@ extern "C" int32_t paged_kv_swap_blocks(const void* src_k, const void* src_v, vo
   if (int32_t e = kernel_address(pairs, "pairs", &pr)) return e;
   const int eb = dt == PKV_BF16 ? 2 : 4;
   const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * eb;
+  int32_t* status = nullptr;
+  if (int32_t e = pkv::device_status_ptr(&status)) return e;
   swap_blocks_kernel<<<dim3(num_pairs, 2), 256, 0, static_cast<hipStream_t>(stream)>>>(
       sk, sv, const_cast<char*>(dk), const_cast<char*>(dv), reinterpret_cast<const int32_t*>(pr), block_bytes,
-      src_num_blocks, dst_num_blocks);
+      src_num_blocks, dst_num_blocks, status);
   return launch_status("paged_kv_swap_blocks");
 }

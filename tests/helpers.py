@@ -90,13 +90,19 @@ BF16_U = 2.0 ** -8
 
 
 def assert_within_prefill_bound(got, ref, absv, what=""):
+    """Prefill output against the fp64 oracle: the decode bar (max abs error
+    <= 2e-3 and max relative error <= 1e-2, relative as in ``errors``) and
+    the elementwise rounding bound above."""
     g = got.float().cpu().double().numpy() if hasattr(got, "cpu") else np.asarray(got, np.float64)
     assert np.isfinite(g).all(), f"{what}: non-finite output"
     err = np.abs(g - ref)
     bound = BF16_U * (absv + np.abs(ref)) + 1e-5 * absv + 1e-7
     worst = float((err / bound).max())
-    say(f"  {what}: max abs {err.max():.3e}, max err/bound {worst:.3f}")
+    tau = 1e-3 * float(np.abs(ref).max()) if ref.size else 0.0
+    rel = float((err / np.maximum(np.abs(ref), max(tau, 1e-300))).max(initial=0.0))
+    say(f"  {what}: max abs {err.max():.3e}, max rel {rel:.3e}, max err/bound {worst:.3f}")
     assert err.max() <= TOL["bf16"]["abs"], f"{what}: max abs error {err.max()} > {TOL['bf16']['abs']}"
+    assert rel <= TOL["bf16"]["rel"], f"{what}: max rel error {rel} > {TOL['bf16']['rel']}"
     assert worst <= 1.0, f"{what}: error exceeds the bf16-probability bound by {worst:.3f}x"
 
 

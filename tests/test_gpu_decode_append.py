@@ -1,7 +1,8 @@
 """paged_attention_decode_append: the step's cache append and decode
 attention in one call (the decode kernel writes the rows itself when there
-is at most one appended row per decode workgroup, else a one-row append
-launch runs first; the cases below take both branches).  Its pools and
+are at most as many sequences as decode workgroups per kv head, else a
+one-row append launch runs first; the cases below take both branches, and
+one folded case puts several sequence ends in one workgroup).  Its pools and
 outputs must equal, bit for bit, those of paged_kv_append (at the slot of
 position L - 1) followed by paged_attention_decode, and its outputs must
 match the oracle within the decode tolerances.  Unused slots hold NaN, so a
@@ -129,17 +130,17 @@ def _two_paths(w, steps):
     return outB, cache
 
 
-def test_70b_32k_full_size_bitwise_and_sampled_oracle():
-    """The 70B-shaped 32k layer at full size in the default launch; sampled
-    sequences against the oracle from their logical tokens."""
+def test_70b_32k_full_size_bitwise_and_oracle():
+    """The 70B-shaped 32k layer at full size in the default launch; every
+    sequence against the oracle from its logical tokens."""
     w = Workload("c3_70b_32k_bf16")
     out, _ = _two_paths(w, steps=2)
     run = OracleRun(w, materialize=False)
     run.step(0)
     run.step(1)
     q = w.q(1)
-    for s in (0, 15):
-        assert_close(out[s].cpu(), run.logical_attention(q, s), "bf16", f"70B 32k seq {s} step 1")
+    ref = np.stack([run.logical_attention(q, s) for s in range(w.num_seqs)])
+    assert_close(out.cpu(), ref, "bf16", "70B 32k, all 16 sequences, step 1")
 
 
 def test_mixed_bs32_full_size_bitwise():
@@ -147,8 +148,8 @@ def test_mixed_bs32_full_size_bitwise():
 
 
 def test_prefix_sharing_with_copy_on_write_bitwise():
-    """400 sequences over a shared prefix (more than one appended row per
-    workgroup: the append launch runs first): the first step copies the
+    """400 sequences over a shared prefix (more sequences than workgroups per
+    kv head: the append launch runs first): the first step copies the
     shared partial blocks before the append writes into the copies."""
     _two_paths(Workload("c4_prefix_bf16"), steps=2)
 
@@ -286,3 +287,78 @@ def test_small_workspace_is_rejected_before_any_launch():
         pkv.paged_attention_decode_append(out, q, kn, kn, k, v, tables, ln, max(lens), workspace=small)
     torch.cuda.synchronize()
     assert torch.equal(k, k0) and torch.equal(v, v0), "a rejected call must not touch the pools"
+
+
+def _ranges(lens, bs, wph):
+    """Blocks [b0, b1) of the per-head block list each decode workgroup takes."""
+    T = sum(-(-L // bs) for L in lens)
+    ng = min(wph, T)
+    return [(k * T // ng, (k + 1) * T // ng) for k in range(ng)]
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_folded_append_with_several_sequence_ends_per_workgroup(bs):
+    """Short sequences packed in front of a long one: the first workgroup's
+    range holds the last block of several sequences, so its segments each
+    write one appended row before their loads.  Bitwise against append then
+    decode, and against the oracle."""
+    import paged_kv_cache_230_amd as pkv
+
+    lens = [1, 3, 17, 40, 5000]
+    Hq, Hkv, d = 64, 8, 128
+    S = len(lens)
+    wph = pkv.paged_attention_workgroups_per_head(S, Hkv, d, bs, max(lens))
+    assert S <= wph, "the append must be folded"
+    starts, ends = [], 0
+    for L in lens:
+        starts.append(ends)
+        ends += -(-L // bs)
+    last_blocks = [st + -(-L // bs) - 1 for st, L in zip(starts, lens)]
+    per_wg = [sum(b0 <= x < b1 for x in last_blocks) for b0, b1 in _ranges(lens, bs, wph)]
+    say(f"case decode_append several ends per workgroup bs{bs}: up to {max(per_wg)} ends in one workgroup")
+    assert max(per_wg) >= 2
+    g = torch.Generator().manual_seed(4242 + bs)
+    nb = sum(-(-L // bs) for L in lens) + 3
+    perm = torch.randperm(nb, generator=g).numpy()
+    maxb = max(-(-L // bs) for L in lens)
+    tables = np.full((S, maxb), -1, np.int32)
+    used = 0
+    for s, L in enumerate(lens):
+        n = -(-L // bs)
+        tables[s, :n] = perm[used:used + n]
+        used += n
+    hist = [(s, t) for s, L in enumerate(lens) for t in range(L - 1)]
+    slots = np.array([int(tables[s, t // bs]) * bs + t % bs for s, t in hist], np.int64)
+    std = 128 ** -0.5
+    kh = (torch.randn(len(hist), Hkv, d, generator=g) * std).to(torch.bfloat16)
+    vh = (torch.randn(len(hist), Hkv, d, generator=g) * std).to(torch.bfloat16)
+    kn = (torch.randn(S, Hkv, d, generator=g) * std).to(torch.bfloat16)
+    vn = (torch.randn(S, Hkv, d, generator=g) * std).to(torch.bfloat16)
+    q = (torch.randn(S, Hq, d, generator=g) * std * 64).to(torch.bfloat16)
+    kA, vA = pkv.new_pools(nb, Hkv, d, bs, torch.bfloat16)
+    kA.fill_(float("nan"))
+    vA.fill_(float("nan"))
+    pkv.paged_kv_append(kh.cuda(), vh.cuda(), kA, vA, torch.from_numpy(slots.astype(np.int32)).cuda())
+    kB, vB = kA.clone(), vA.clone()
+    tab = torch.from_numpy(tables).cuda()
+    ln = torch.tensor(lens, dtype=torch.int32).cuda()
+    new_slots = np.array([int(tables[s, (L - 1) // bs]) * bs + (L - 1) % bs for s, L in enumerate(lens)], np.int64)
+    outA = torch.empty(S, Hq, d, dtype=torch.bfloat16, device="cuda")
+    pkv.paged_kv_append(kn.cuda(), vn.cuda(), kA, vA, torch.from_numpy(new_slots.astype(np.int32)).cuda())
+    pkv.paged_attention_decode(outA, q.cuda(), kA, vA, tab, ln, max(lens))
+    outB = torch.empty_like(outA)
+    pkv.device_status()
+    pkv.paged_attention_decode_append(outB, q.cuda(), kn.cuda(), vn.cuda(), kB, vB, tab, ln, max(lens))
+    assert pkv.device_status() == 0
+    torch.cuda.synchronize()
+    assert _bits_equal(kA, kB) and _bits_equal(vA, vB), "pools differ from append + decode"
+    assert _bits_equal(outA, outB), "outputs differ from append + decode"
+    ok, ov = opool.new_pools(nb, Hkv, d, bs, np.uint16)
+
+    def st(t):
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    opool.append(ok, ov, np.concatenate([st(kh), st(kn)]), np.concatenate([st(vh), st(vn)]),
+                 np.concatenate([slots, new_slots]))
+    ref = oatt.decode_attention(st(q), ok, ov, tables, np.array(lens))
+    assert_close(outB, ref, "bf16", f"decode_append several ends bs{bs}")
