@@ -244,6 +244,27 @@ int32_t paged_attention_decode_append(void* out, const void* q, const void* k_ne
                                       float scale, int32_t partition_size, void* workspace,
                                       size_t workspace_bytes, pkv_dtype dt, void* stream);
 
+/* paged_attention_decode_append without a caller workspace, for callers */
+/* that cannot allocate device memory (code under HIP graph capture,      */
+/* serving loops that forbid allocation): the call allocates nothing and  */
+/* uses a scratch array built into the library instead, 32 MiB per GPU,   */
+/* held by every GPU the library runs on until the process ends.  That is */
+/* enough for the default partition_size = 0 on every supported shape up */
+/* to several thousand sequences; a request whose workspace              */
+/* (paged_attention_workspace_bytes at the device's occupancy) exceeds it */
+/* fails with PKV_ERR_CAPACITY before any launch.  Every call on one GPU  */
+/* shares that GPU's array (no content carries over between calls: each */
+/* call writes what it reads), so calls that overlap on one GPU, e.g. on */
+/* two streams, race; order them on one stream.  Arguments, results and  */
+/* other errors are those of paged_attention_decode_append.               */
+int32_t paged_attention_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                                              void* k_cache, void* v_cache, const int32_t* block_tables,
+                                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                                              int32_t max_context_len, float scale, int32_t partition_size,
+                                              pkv_dtype dt, void* stream);
+
 /* Workgroups per kv head that paged_attention_decode uses for these     */
 /* arguments on the current device, or a negative status.                 */
 int32_t paged_attention_workgroups_per_head(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,

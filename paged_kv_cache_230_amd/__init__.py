@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     new_pools,
     paged_attention_decode,
     paged_attention_decode_append,
+    paged_attention_decode_append_noalloc,
     paged_attention_prefill,
     paged_attention_workgroups_per_head,
     paged_attention_workspace_bytes,

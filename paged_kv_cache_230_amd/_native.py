@@ -83,6 +83,11 @@ _SIGS = {
         [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
          _sz, _i32, _vp],
     ),
+    "paged_attention_decode_append_noalloc": (
+        _i32,
+        [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+         _vp],
+    ),
     "paged_attention_workgroups_per_head": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attention_prefill": (

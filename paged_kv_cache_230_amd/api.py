@@ -26,6 +26,7 @@ __all__ = [
     "paged_kv_copy_blocks",
     "paged_attention_decode",
     "paged_attention_decode_append",
+    "paged_attention_decode_append_noalloc",
     "paged_attention_workspace_bytes",
     "paged_attention_workgroups_per_head",
     "BlockManager",
@@ -238,6 +239,37 @@ def paged_attention_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_
             _ptr(context_lens), S, Hq, H, d, bs, nb, block_tables.shape[1], int(max_context_len), float(scale),
             int(partition_size), _ptr(workspace), workspace.numel() if workspace is not None else 0,
             _dt(k_cache.dtype), _stream(dev),
+        )
+    )
+    return out
+
+
+def paged_attention_decode_append_noalloc(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                          max_context_len, scale=None, partition_size=0):
+    """:func:`paged_attention_decode_append` with the library's built-in
+    scratch instead of a workspace: the call allocates no device memory."""
+    nb, H, d, bs = _pool_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    _need(out, "out", k_cache.dtype, dev, 3)
+    _need(k_new, "k_new", k_cache.dtype, dev, 3)
+    _need(v_new, "v_new", k_cache.dtype, dev, 3)
+    _need(block_tables, "block_tables", torch.int32, dev, 2)
+    _need(context_lens, "context_lens", torch.int32, dev, 1)
+    S, Hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (S, Hq, d):
+        raise ValueError("q/out must be [num_seqs][num_q_heads][head_dim]")
+    if tuple(k_new.shape) != (S, H, d) or tuple(v_new.shape) != (S, H, d):
+        raise ValueError("k_new/v_new must be [num_seqs][num_kv_heads][head_dim]")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables/context_lens must have num_seqs rows")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    N.check(
+        N.lib.paged_attention_decode_append_noalloc(
+            _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), S, Hq, H, d, bs, nb, block_tables.shape[1], int(max_context_len), float(scale),
+            int(partition_size), _dt(k_cache.dtype), _stream(dev),
         )
     )
     return out

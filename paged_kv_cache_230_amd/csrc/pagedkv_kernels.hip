@@ -1332,6 +1332,37 @@ int32_t decode_call(void* out, const void* q, const void* k_new, const void* v_n
   return launch_status(what);
 }
 
+// Scratch of the allocation-free decode call: the decode workspace (piece
+// records and partials) of one call, held by every GPU the library runs on
+// until the process ends.  Host code never names the array itself (its
+// name is a host-side stand-in, not a device address); it uses the address
+// scratch_ptr returns for the current device.
+constexpr size_t kScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of the current GPU's scratch array, looked up once per
+// device with that device current.
+int32_t scratch_ptr(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return pkv::fail(PKV_ERR_DEVICE, "no usable current device for the decode scratch");
+  }
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return pkv::fail(PKV_ERR_DEVICE, "decode scratch address: %s", hipGetErrorString(e));
+    }
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1357,6 +1388,31 @@ int32_t paged_attention_decode_append(void* out, const void* q, const void* k_ne
   return decode_call(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
                      partition_size, workspace, workspace_bytes, dt, stream, "paged_attention_decode_append");
+}
+
+int32_t paged_attention_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                                              void* k_cache, void* v_cache, const int32_t* block_tables,
+                                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                              float scale, int32_t partition_size, pkv_dtype dt, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (num_seqs <= 0)  // validation only; nothing to launch
+    return decode_call(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                       partition_size, nullptr, 0, dt, stream, "paged_attention_decode_append_noalloc");
+  void* ws = nullptr;
+  if (int32_t e = scratch_ptr(&ws)) return e;
+  // decode_call rejects a request whose workspace exceeds the scratch with
+  // PKV_ERR_CAPACITY before launching anything.
+  const int32_t st = decode_call(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                                 num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                 max_context_len, scale, partition_size, ws, kScratchBytes, dt, stream,
+                                 "paged_attention_decode_append_noalloc");
+  if (st == PKV_ERR_CAPACITY)
+    pkv::fail(PKV_ERR_CAPACITY, "paged_attention_decode_append_noalloc: %s (the built-in scratch holds %zu bytes)",
+              pkv_last_error(), kScratchBytes);
+  return st;
 }
 
 }  // extern "C"
