@@ -16,7 +16,9 @@ import os
 import torch  # noqa: F401
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpagedkv.so")
+# PKV_LIB_PATH loads another build of the library instead of the in-tree one
+# (the tests use it for a host-only sanitizer build of the block manager).
+LIB_PATH = os.environ.get("PKV_LIB_PATH") or os.path.join(HERE, "libpagedkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = -1

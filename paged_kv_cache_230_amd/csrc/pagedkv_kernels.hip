@@ -1048,23 +1048,20 @@ std::string& last_error_slot() {
 }
 
 int32_t stage_device_ptr(const int32_t* stage, const int32_t** dev_out) {
-  // Cached for the last buffers seen (callers alternate a few stage buffers).
-  thread_local const void* host[4] = {nullptr, nullptr, nullptr, nullptr};
-  thread_local void* dev[4] = {nullptr, nullptr, nullptr, nullptr};
-  thread_local int next = 0;
-  for (int i = 0; i < 4; ++i)
-    if (host[i] == stage) {
-      *dev_out = static_cast<const int32_t*>(dev[i]);
-      return PKV_OK;
-    }
+  // Looked up on every call (nothing is cached): a pinned buffer may be
+  // freed and its address reused by pageable memory, which the GPU cannot
+  // read.  Both queries are host-side table lookups, microseconds against
+  // a decode step.
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, stage) != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_INVALID_ARG, "stage buffer is not pinned host memory (hipHostMalloc / pin_memory)");
+  }
   void* d = nullptr;
   if (hipHostGetDevicePointer(&d, const_cast<int32_t*>(stage), 0) != hipSuccess || !d) {
     (void)hipGetLastError();
     return fail(PKV_ERR_INVALID_ARG, "stage buffer is not pinned host memory (hipHostMalloc / pin_memory)");
   }
-  host[next] = stage;
-  dev[next] = d;
-  next = (next + 1) & 3;
   *dev_out = static_cast<const int32_t*>(d);
   return PKV_OK;
 }

@@ -105,11 +105,23 @@ def test_stage_step_rejects_unpinned_stage_without_side_effects():
 
     host = np.zeros(64, np.int32)  # pageable memory
     ids = np.zeros(1, np.int64)
-    code = N.lib.pkv_bm_stage_step(bm._h, ids.ctypes.data_as(C.POINTER(C.c_int64)), 1, None, C.c_void_p(host.ctypes.data),
-                                   64, C.c_void_p(t.data_ptr()), 4, C.c_void_p(v.data_ptr()), C.c_void_p(v.data_ptr()),
-                                   C.c_void_p(p.data_ptr()), 1, 0, None, None, None)
+
+    def stage(addr):
+        return N.lib.pkv_bm_stage_step(bm._h, ids.ctypes.data_as(C.POINTER(C.c_int64)), 1, None, C.c_void_p(addr),
+                                       64, C.c_void_p(t.data_ptr()), 4, C.c_void_p(v.data_ptr()),
+                                       C.c_void_p(v.data_ptr()), C.c_void_p(p.data_ptr()), 1, 0, None, None, None)
+
+    code = stage(host.ctypes.data)
     assert code == N.PKV_ERR_INVALID_ARG and "pinned" in N.last_error()
     assert bm.seq_len(0) == 0 and bm.num_free() == 16
+    # A pinned record works; a pageable one right after it is still checked
+    # (the library keeps no mapping from one call to the next), and the
+    # pinned one works again.
+    pinned = torch.zeros(64, dtype=torch.int32, pin_memory=True)
+    assert stage(pinned.data_ptr()) == 0 and bm.seq_len(0) == 1
+    assert stage(host.ctypes.data) == N.PKV_ERR_INVALID_ARG and bm.seq_len(0) == 1
+    assert stage(pinned.data_ptr()) == 0 and bm.seq_len(0) == 2
+    torch.cuda.synchronize()
 
 
 def test_decode_through_staged_buffers_matches_oracle():
