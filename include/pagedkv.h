@@ -436,10 +436,14 @@ int32_t pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids,
 /*   cow_pairs [n][2] (the copies to run before writing the tokens),      */
 /*   block_tables [n_seqs][max_blocks_per_seq]: only the entries that     */
 /*   changed since the last call on the same table are written (new       */
-/*   blocks, copy-on-write replacements, sequences that moved rows); the  */
-/*   first call on a table, a different table or width, or full != 0     */
-/*   writes every used entry.  Entries past ceil(L / bs) are not written. */
-/* The table must only be written by this function between calls.        */
+/*   blocks, copy-on-write replacements, sequences that moved rows).  The */
+/*   manager tracks two device tables, so a caller may alternate two      */
+/*   buffer sets (stage step k+1 into one while step k still reads the    */
+/*   other, e.g. on a second stream); the first call on a table, a third  */
+/*   table (it replaces the least recently used one), another width, or   */
+/*   full != 0 writes every used entry.  Entries past ceil(L / bs) are    */
+/*   not written.                                                          */
+/* A table must only be written by this function between calls.           */
 /* token_ids     : host [n_seqs], the new tokens' ids, or NULL (as in     */
 /*                 pkv_bm_append_slots)                                   */
 /* stage         : pinned host memory (hipHostMalloc / pinned tensor) of  */

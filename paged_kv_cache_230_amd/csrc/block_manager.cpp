@@ -71,12 +71,13 @@ struct pkv_block_manager {
     // Swapped out: the table is empty and host_table holds the host blocks.
     bool swapped = false;
     std::vector<int32_t> host_table;
-    // Device mirror (pkv_bm_stage_step): row of the device table this
-    // sequence was last written to (-1: none), entries written there, and the
-    // lowest entry changed since (a copy-on-write replacement).
-    int32_t mirror_row = -1;
-    int32_t mirror_blocks = 0;
-    int32_t dirty_from = INT32_MAX;
+    // Device mirrors (pkv_bm_stage_step), one per tracked device table: row
+    // of that table this sequence was last written to (-1: none), entries
+    // written there, and the lowest entry changed since (a copy-on-write
+    // replacement).
+    int32_t mirror_row[2] = {-1, -1};
+    int32_t mirror_blocks[2] = {0, 0};
+    int32_t dirty_from[2] = {INT32_MAX, INT32_MAX};
   };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
@@ -94,11 +95,18 @@ struct pkv_block_manager {
   // Host swap pool.
   int32_t num_host_blocks = 0;
   std::vector<int32_t> host_free;  // back() is handed out next
-  // Device table the mirror state refers to, and the sequence whose entries
-  // each of its rows last received.
-  const void* mirror_table = nullptr;
-  int32_t mirror_width = 0;
-  std::vector<int64_t> row_owner;
+  // The device tables the mirror state refers to (a caller may alternate two,
+  // e.g. to stage one step while the previous one still reads the other),
+  // with the sequence whose entries each row last received, and the call
+  // count of their last use (the least recently used one is replaced).
+  struct DeviceTable {
+    const void* table = nullptr;
+    int32_t width = 0;
+    std::vector<int64_t> row_owner;
+    uint64_t last_use = 0;
+  };
+  DeviceTable mirrors[2];
+  uint64_t stage_calls = 0;
   // Scratch reused by pkv_bm_stage_step and pkv_bm_append_slots.
   std::vector<int32_t> scratch_slots, scratch_pairs, scratch_released;
 };
@@ -389,7 +397,8 @@ int32_t pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32
           if (--bm->refcount[old] == 0) released.push_back(old);  // registered; last holder gone
           bm->refcount[b] = 1;
           s.table[L / bs] = b;
-          if (L / bs < s.dirty_from) s.dirty_from = L / bs;
+          for (int32_t& d : s.dirty_from)
+            if (L / bs < d) d = L / bs;
         }
       }
       if (token_ids && static_cast<int64_t>(s.tokens.size()) == L) s.tokens.push_back(token_ids[ns]);
@@ -535,7 +544,7 @@ int32_t pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs_ou
   release_table(bm, q.table);
   q.table.clear();
   q.swapped = true;
-  q.mirror_row = -1;  // its device-table row is rewritten in full after swap-in
+  q.mirror_row[0] = q.mirror_row[1] = -1;  // its device-table rows are rewritten in full after swap-in
   if (n_pairs_out) *n_pairs_out = n;
   return pkv::ok();
 }
@@ -563,7 +572,7 @@ int32_t pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs_out
   for (int32_t h : q.host_table) bm->host_free.push_back(h);
   q.host_table.clear();
   q.swapped = false;
-  q.mirror_row = -1;
+  q.mirror_row[0] = q.mirror_row[1] = -1;
   if (n_pairs_out) *n_pairs_out = n;
   return pkv::ok();
 }
@@ -609,7 +618,14 @@ int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t
   const int32_t* stage_dev = nullptr;
   if (int32_t e = pkv::stage_device_ptr(stage, &stage_dev)) return e;
   const int32_t bs = bm->block_size;
-  const bool remap = full || bm->mirror_table != block_tables || bm->mirror_width != max_blocks_per_seq;
+  // The mirror of this device table, or the least recently used one, which
+  // is then rebuilt (every entry written).
+  int m = -1;
+  for (int k = 0; k < 2; ++k)
+    if (bm->mirrors[k].table == block_tables && bm->mirrors[k].width == max_blocks_per_seq) m = k;
+  bool remap = full || m < 0;
+  if (m < 0) m = bm->mirrors[0].last_use <= bm->mirrors[1].last_use ? 0 : 1;
+  auto& mt = bm->mirrors[m];
 
   // Bound the record before anything changes, so every failure leaves the
   // manager untouched (the append below validates ids and counts the rest).
@@ -619,16 +635,16 @@ int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t
     if (it == bm->seqs.end()) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
     if (int32_t e = check_on_gpu(it->second, seq_ids[i])) return e;
     const auto& q = it->second;
-    const bool owned = !remap && q.mirror_row == i && i < static_cast<int32_t>(bm->row_owner.size()) &&
-                       bm->row_owner[i] == seq_ids[i];
+    const bool owned = !remap && q.mirror_row[m] == i && i < static_cast<int32_t>(mt.row_owner.size()) &&
+                       mt.row_owner[i] == seq_ids[i];
     const int64_t nb_after = (static_cast<int64_t>(q.len) + 1 + bs - 1) / bs;
     if (nb_after > max_blocks_per_seq)
       return pkv::fail(PKV_ERR_CAPACITY, "sequence %lld would hold %lld blocks > max_blocks_per_seq %d",
                        (long long)seq_ids[i], (long long)nb_after, max_blocks_per_seq);
     int64_t from = 0;
     if (owned) {
-      from = q.mirror_blocks;
-      if (q.dirty_from < from) from = q.dirty_from;
+      from = q.mirror_blocks[m];
+      if (q.dirty_from[m] < from) from = q.dirty_from[m];
       const int64_t write_at = q.len / bs;  // a copy-on-write may replace this entry
       if (write_at < from) from = write_at;
     }
@@ -651,18 +667,18 @@ int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t
   int32_t* pairs = lens + n_seqs;
   int32_t* upd = pairs + 2 * nc;
   int32_t nu = 0, max_len = 0;
-  if (remap) bm->row_owner.clear();
-  if (static_cast<int32_t>(bm->row_owner.size()) < n_seqs) bm->row_owner.resize(n_seqs, -1);
+  if (remap) mt.row_owner.clear();
+  if (static_cast<int32_t>(mt.row_owner.size()) < n_seqs) mt.row_owner.resize(n_seqs, -1);
   for (int32_t i = 0; i < n_seqs; ++i) {
     auto& q = bm->seqs.find(seq_ids[i])->second;
-    const bool owned = !remap && q.mirror_row == i && bm->row_owner[i] == seq_ids[i];
+    const bool owned = !remap && q.mirror_row[m] == i && mt.row_owner[i] == seq_ids[i];
     slots[i] = bm->scratch_slots[i];
     lens[i] = q.len;
     if (q.len > max_len) max_len = q.len;
     const int32_t nb = static_cast<int32_t>(q.table.size());
     int32_t from = 0;
     if (owned) {
-      from = q.mirror_blocks < q.dirty_from ? q.mirror_blocks : q.dirty_from;
+      from = q.mirror_blocks[m] < q.dirty_from[m] ? q.mirror_blocks[m] : q.dirty_from[m];
       if (from > nb) from = nb;
     }
     for (int32_t c = from; c < nb; ++c) {
@@ -671,10 +687,10 @@ int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t
       upd[3 * nu + 2] = q.table[c];
       ++nu;
     }
-    q.mirror_row = i;
-    q.mirror_blocks = nb;
-    q.dirty_from = INT32_MAX;
-    bm->row_owner[i] = seq_ids[i];
+    q.mirror_row[m] = i;
+    q.mirror_blocks[m] = nb;
+    q.dirty_from[m] = INT32_MAX;
+    mt.row_owner[i] = seq_ids[i];
   }
   for (int32_t k = 0; k < 2 * nc; ++k) pairs[k] = bm->scratch_pairs[k];
   stage[0] = n_seqs;
@@ -682,9 +698,10 @@ int32_t pkv_bm_stage_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t
   stage[2] = nu;
   stage[3] = max_blocks_per_seq;
   if (remap) {
-    bm->mirror_table = block_tables;
-    bm->mirror_width = max_blocks_per_seq;
+    mt.table = block_tables;
+    mt.width = max_blocks_per_seq;
   }
+  mt.last_use = ++bm->stage_calls;
   if (int32_t e = pkv::launch_stage(stage_dev, n_seqs, nc, nu, max_blocks_per_seq, slot_mapping, context_lens,
                                     cow_pairs, block_tables, stream))
     return e;

@@ -152,3 +152,32 @@ def test_decode_through_staged_buffers_matches_oracle():
         say(f"  staged step {k}: {n_cow} copy pairs, max_len {max_len}")
         assert np.array_equal(storage_np(out), storage_np(out2))
         assert_close(out, run.attention(q), "bf16", f"staged decode step {k}")
+
+
+def test_stage_step_alternating_two_tables():
+    """Two buffer sets used on alternate steps (as when step k+1 is staged
+    while step k still reads the other set): each table receives only the
+    entries changed since its own last update, and must equal the model's
+    tables at every step, through row reorders, copy-on-write and a third
+    table that replaces the least recently used one."""
+    w = Workload("c4_prefix_bf16", overrides=dict(num_prompts=5, n_samples=4, prefix_len=96, suffix_max=40,
+                                                   num_blocks=600))
+    cache = product_cache(w)
+    model = OracleRun(w, materialize=False).bm
+    seqs = list(w.decode_seqs)
+    n = len(seqs)
+    maxb = 64
+    sets = [Staged(n, maxb), Staged(n, maxb)]
+    rng = np.random.default_rng(11)
+    n_cow_total = 0
+    for k in range(36):
+        st = sets[k % 2]
+        if k == 20:  # a third table in place of this set's: it replaces the older mirror
+            st.new_tables(n)
+        order = seqs if k % 7 else [seqs[i] for i in rng.permutation(n)]
+        n_cow, max_len = st.step(cache.bm, order)
+        slots_m, pairs_m = model.append_slots(order)
+        n_cow_total += n_cow
+        _check(st, order, model, slots_m, pairs_m, n_cow, f"step {k} (set {k % 2})")
+    assert n_cow_total > 0, "the workload must exercise copy-on-write"
+    model.check_invariants()
