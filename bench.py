@@ -142,7 +142,7 @@ def measured_read_peak(dev, nbytes=4 << 30, reps=6):
 
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.fill_(1)
-    sink = torch.empty(2048 * 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)  # workgroups
     pkv.stream_read(buf, sink)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     ev[0].record()
@@ -730,6 +730,8 @@ def main():
                     help="append with paged_kv_append, then paged_attention_decode (two calls) instead of "
                          "paged_attention_decode_append")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences in the oracle sample (default: all)")
+    ap.add_argument("--no-read-peak", action="store_true",
+                    help="skip the streaming-read probe (for counter runs, which would count its reads too)")
     ap.add_argument("--overlap-stage", action="store_true",
                     help="stage step k+1's bookkeeping on a second stream during step k's decode (two buffer sets)")
     ap.add_argument("--marked", type=int, default=50,
@@ -932,7 +934,7 @@ def main():
     step_kv = [decode_kv_bytes(step_lens[dk[i]], c.num_kv_heads, c.head_dim, c.elem_bytes) for i in range(1, len(dk))]
     step_gbps = [b / (t * 1e-6) / 1e9 for b, t in zip(step_kv, step_us)]
     dec_us = [1e3 * t for t in dec_ms]
-    peak_read, median_read = measured_read_peak(dev)
+    peak_read, median_read = (None, None) if args.no_read_peak else measured_read_peak(dev)
     ms_per_step = elapsed / args.steps * 1e3
     value = sum(kv_bytes) / elapsed / 1e9
     traffic = load_traffic(w.name, P) if not args.separate_append else None
@@ -989,9 +991,9 @@ def main():
             "unique_kv_block_bytes_last_call": unique_blocks * block_bytes,
             "calls_timed": len(dec_ms),
             "call_us": {k: round(v, 2) for k, v in percentiles(dec_us).items()},
-            "measured_read_peak_gbps": round(peak_read / 1e9, 1),
-            "measured_read_median_gbps": round(median_read / 1e9, 1),
-            "frac_of_measured_peak": round(achieved / peak_read, 4),
+            "measured_read_peak_gbps": round(peak_read / 1e9, 1) if peak_read else None,
+            "measured_read_median_gbps": round(median_read / 1e9, 1) if median_read else None,
+            "frac_of_measured_peak": round(achieved / peak_read, 4) if peak_read else None,
         },
         "step_distribution": {
             "steps": len(step_us),

@@ -271,6 +271,17 @@ int32_t paged_attention_workgroups_per_head(int32_t num_seqs, int32_t num_kv_hea
                                             int32_t block_size, int32_t max_context_len, int32_t partition_size,
                                             pkv_dtype dt);
 
+/* Fixed charge per sequence, in blocks, in the decode kernel's split of  */
+/* a kv head's work ("PagedAttention" (robocikowo.com), Komponenty: the    */
+/* kernel walks each sequence's block table): the blocks of all sequences */
+/* form one list in which every non-empty sequence also counts this many  */
+/* blocks for its fixed work (table read, query load, first K/V round     */
+/* trip, cross-wave merge), and each of the W workgroups of the head      */
+/* (paged_attention_workgroups_per_head) takes an equal contiguous range  */
+/* of the list's C positions, [k C / W, (k+1) C / W).  block_size is 16   */
+/* or 32; returns a negative status otherwise.                            */
+int32_t paged_attention_segment_cost(int32_t block_size);
+
 /* Workspace bytes paged_attention_decode needs for these arguments on    */
 /* the current device (0 only when num_seqs == 0).  Returns 0 and sets    */
 /* the last error for invalid arguments.                                   */

@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     paged_attention_decode_append,
     paged_attention_decode_append_noalloc,
     paged_attention_prefill,
+    paged_attention_segment_cost,
     paged_attention_workgroups_per_head,
     paged_attention_workspace_bytes,
     paged_kv_append,

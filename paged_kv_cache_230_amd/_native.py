@@ -91,6 +91,7 @@ _SIGS = {
          _vp],
     ),
     "paged_attention_workgroups_per_head": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "paged_attention_segment_cost": (_i32, [_i32]),
     "paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attention_prefill": (
         _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,

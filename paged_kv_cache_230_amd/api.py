@@ -29,6 +29,7 @@ __all__ = [
     "paged_attention_decode_append_noalloc",
     "paged_attention_workspace_bytes",
     "paged_attention_workgroups_per_head",
+    "paged_attention_segment_cost",
     "BlockManager",
     "device_status",
     "stream_read",
@@ -155,6 +156,12 @@ def paged_attention_workgroups_per_head(num_seqs, num_kv_heads, head_dim, block_
                                         partition_size=0, dtype=torch.bfloat16):
     return N.check(N.lib.paged_attention_workgroups_per_head(num_seqs, num_kv_heads, head_dim, block_size,
                                                              max_context_len, partition_size, _dt(dtype)))
+
+
+def paged_attention_segment_cost(block_size):
+    """Blocks each non-empty sequence is charged for its fixed work in the
+    decode kernel's balanced split of a kv head's block list."""
+    return N.check(N.lib.paged_attention_segment_cost(block_size))
 
 
 def paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,

@@ -99,6 +99,7 @@ struct DecodeArgs {
   int32_t* meta;     // [S][Hkv][2] first workgroup index and number of pieces of (s, g)
   int32_t* status;   // device status word
   int32_t wgs_per_head;  // N / Hkv
+  int32_t seg_cost;      // fixed cost of one segment in the balanced split, in blocks
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -211,6 +212,7 @@ struct DecodeSmem {
   // hold them in scalar registers through the step loop
   const void* append_src[2];
   int ids[kIdChunk];  // block ids of the current chunk of the segment
+  int lens[kThreads];  // raw context lengths, when the batch has at most kThreads sequences
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
@@ -478,10 +480,18 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
       }
   };
 
-  // The wave walks its blocks j = w, w + 4, ... in steps of 16 tokens (two
-  // steps per block when BS = 32), loading step n+1 while computing step n.
-  // Block ids come through LDS, kIdChunk at a time.
+  // The segment's tokens are cut into 16-token units (two per block when
+  // BS = 32) dealt to the waves round robin: wave w takes units w, w + 4,
+  // ..., loading unit n+1 while computing unit n.  With BS = 32 the two
+  // halves of a block go to waves 2i and 2i+1, which load them at about the
+  // same time; a 64-byte V row (one dimension, 32 tokens) is then read by
+  // both halves together, not by one wave a whole step after the other,
+  // which in a saturated stream lets the line leave L2 in between and be
+  // fetched again.  Block ids come through LDS, kIdChunk at a time.
   constexpr int HALVES = BS / 16;
+  static_assert(kWaves % HALVES == 0, "a wave keeps the same half of every block it visits");
+  const int h = w % HALVES;
+  const int nunits = (end - start + 15) / 16;
   auto stage_ids = [&](int c0) {
     const int cn = nblk - c0 < kIdChunk ? nblk - c0 : kIdChunk;
     for (int i = threadIdx.x; i < cn; i += kThreads) {
@@ -506,38 +516,29 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
     const int cn = nblk - c0 < kIdChunk ? nblk - c0 : kIdChunk;
     if (c0 > 0) stage_ids(c0);
     __syncthreads();
+    // units [c0 * HALVES, uend) lie in this chunk's blocks; each holds at
+    // least one valid token
+    const int uend = c0 * HALVES + (min(start + (c0 + cn) * BS, end) - (start + c0 * BS) + 15) / 16;
     Step<BF16, D> st, nxt;
     const void* kt = nullptr;
     const void* vt = nullptr;
-    int j = c0 + w;
-    int h = 0;
-    const int jend = c0 + cn;
-    if (j < jend) {
-      tile_ptrs(j - c0, kt, vt);
-      load_step<BF16, D, BS>(st, kt, vt, 0, row, quad);
-      // Every loop trip issues the next step's loads unconditionally, so the
-      // wait before the current step's math covers only its own loads; the
-      // last step runs after the loop.
+    int u = c0 * HALVES + w;
+    if (u < uend) {
+      tile_ptrs(u / HALVES - c0, kt, vt);
+      load_step<BF16, D, BS>(st, kt, vt, h, row, quad);
+      // Every loop trip issues the next unit's loads unconditionally, so the
+      // wait before the current unit's math covers only its own loads; the
+      // last unit runs after the loop.
       for (;;) {
-        int jn = j;
-        int hn = h + 1;
-        const void* ktn = kt;
-        const void* vtn = vt;
-        if (hn == HALVES || start + j * BS + 16 * hn >= end) {  // wave-uniform
-          hn = 0;
-          jn = j + kWaves;
-        }
-        if (jn >= jend) break;
-        if (hn == 0) tile_ptrs(jn - c0, ktn, vtn);
-        load_step<BF16, D, BS>(nxt, ktn, vtn, hn, row, quad);
-        compute_step(st, start + j * BS + 16 * h);
+        const int un = u + kWaves;
+        if (un >= uend) break;
+        tile_ptrs(un / HALVES - c0, kt, vt);
+        load_step<BF16, D, BS>(nxt, kt, vt, h, row, quad);
+        compute_step(st, start + 16 * u);
         st = nxt;
-        j = jn;
-        h = hn;
-        kt = ktn;
-        vt = vtn;
+        u = un;
       }
-      compute_step(st, start + j * BS + 16 * h);
+      compute_step(st, start + 16 * u);
     }
     __syncthreads();  // sm.ids is rewritten by the next chunk
   }
@@ -551,7 +552,7 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc.o[nt][v] += shfl_xor_f(acc.o[nt][v], 32);
   }
-  const int nw = nblk < kWaves ? nblk : kWaves;
+  const int nw = nunits < kWaves ? nunits : kWaves;  // waves that took at least one unit
   if (w < nw) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -598,15 +599,18 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
 }
 
 // Balanced split.  For one kv head, the blocks of all sequences form one
-// list of T blocks (sequence after sequence).  Workgroup b serves kv head
-// g = b mod H_kv and takes the contiguous range [k T / N_g, (k+1) T / N_g)
-// of that list, k = b / H_kv: every workgroup gets the same number of
-// blocks whatever the mix of lengths.  Within its range it walks segment by
-// segment (one per sequence touched): a segment that is a whole sequence
-// writes its output rows; a piece of a split sequence writes a partial, and
-// the workgroup holding the sequence's first block records (first
-// workgroup, number of pieces) for the merge kernel.  With 8 kv heads the
-// round-robin dealing of workgroups to the 8 XCDs gives each XCD one head.
+// list (sequence after sequence) in which every non-empty sequence is also
+// charged seg_cost blocks' worth of fixed work: C = T + seg_cost x (non-empty
+// sequences).  Workgroup b serves kv head g = b mod H_kv and takes the
+// contiguous range [k C / N_g, (k+1) C / N_g) of that list, k = b / H_kv:
+// every workgroup gets the same amount of work whatever the mix of lengths,
+// and one whose range holds many short sequences gets fewer blocks for the
+// segments it has to set up.  Within its range it walks segment by segment
+// (one per sequence touched): a segment that is a whole sequence writes its
+// output rows; a piece of a split sequence writes a partial, and the
+// workgroup holding the sequence's first block records (first workgroup,
+// number of pieces) for the merge kernel.  With 8 kv heads the round-robin
+// dealing of workgroups to the 8 XCDs gives each XCD one head.
 // Minimum waves per SIMD the compiler must leave room for: 3 for bf16 (142
 // VGPRs at head_dim 128, no spills); fp32 keeps its natural allocation.
 template <bool BF16>
@@ -626,72 +630,108 @@ __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel
     sm.append_src[1] = a.v_new;
   }  // ordered before the reads by the barriers of the length scans
 
-  // Total blocks per head.
-  int T = 0;
-  for (int base = 0; base < S; base += kThreads) {
-    const int s = base + threadIdx.x;
-    int nb = 0;
-    if (s < S) {
-      const int Lr = a.context_lens[s];
+  // Cost of the head's list: each non-empty sequence counts its blocks plus
+  // seg_cost, the fixed work of one segment (block ids, query, first loads,
+  // cross-wave merge) in block units.
+  auto cost_of = [&](int nb) { return nb > 0 ? nb + a.seg_cost : 0; };
+  auto blocks_of = [&](int Lr) { return (clamp_len(Lr, a.max_context_len) + BS - 1) / BS; };
+  // Sequence s holds [pre, pre + cost) of the list: the charge first, then
+  // its blocks at [pre + seg_cost, pre + cost).  The first sequence touched
+  // is the one whose interval holds c0.
+  const bool small = S <= kThreads;
+  int C = 0, s = 0, pre = 0;
+  int64_t c0 = 0, c1 = 0;
+  if (small) {
+    // One scan: each thread keeps its sequence's inclusive prefix, and the
+    // lengths stay in LDS for the walk.
+    const int sq = threadIdx.x;
+    int cst = 0;
+    if (sq < S) {
+      const int Lr = a.context_lens[sq];
       if ((Lr < 0 || Lr > a.max_context_len) && k == 0) report(a.status, PKV_DEV_BAD_LENGTH);
-      nb = (clamp_len(Lr, a.max_context_len) + BS - 1) / BS;
+      sm.lens[sq] = Lr;
+      cst = cost_of(blocks_of(Lr));
     }
-    int tot;
-    block_scan<BF16, D>(nb, &tot, sm);
-    T += tot;
-  }
-  const int Ng = a.wgs_per_head < T ? a.wgs_per_head : T;  // at least one block per workgroup
-  if (k >= Ng) return;
-  const int64_t b0 = static_cast<int64_t>(k) * T / Ng;
-  const int64_t b1 = static_cast<int64_t>(k + 1) * T / Ng;
-
-  // First sequence touched: prefix(s) <= b0 < prefix(s) + nb(s).
-  int s = 0, pre = 0, run = 0;
-  for (int base = 0; base < S; base += kThreads) {
     if (threadIdx.x == 0) sm.found_seq = -1;
-    const int sq = base + threadIdx.x;
-    const int nb = sq < S ? (clamp_len(a.context_lens[sq], a.max_context_len) + BS - 1) / BS : 0;
-    int tot;
-    const int incl = run + block_scan<BF16, D>(nb, &tot, sm);
-    if (sq < S && nb > 0 && incl > b0 && incl - nb <= b0) {
+    const int incl = block_scan<BF16, D>(cst, &C, sm);
+    const int Ng = a.wgs_per_head < C ? a.wgs_per_head : C;
+    if (k >= Ng) return;  // workgroup-uniform
+    c0 = static_cast<int64_t>(k) * C / Ng;
+    c1 = static_cast<int64_t>(k + 1) * C / Ng;
+    if (cst > 0 && incl > c0 && incl - cst <= c0) {
       sm.found_seq = sq;
-      sm.found_pre = incl - nb;
+      sm.found_pre = incl - cst;
     }
     __syncthreads();
-    const int fs = sm.found_seq;
-    const int fp = sm.found_pre;
-    __syncthreads();
-    if (fs >= 0) {
-      s = fs;
-      pre = fp;
-      break;
+    s = sm.found_seq;  // found: c0 < C lies in one sequence's interval
+    pre = sm.found_pre;
+  } else {
+    for (int base = 0; base < S; base += kThreads) {
+      const int sq = base + threadIdx.x;
+      int cst = 0;
+      if (sq < S) {
+        const int Lr = a.context_lens[sq];
+        if ((Lr < 0 || Lr > a.max_context_len) && k == 0) report(a.status, PKV_DEV_BAD_LENGTH);
+        cst = cost_of(blocks_of(Lr));
+      }
+      int tot;
+      block_scan<BF16, D>(cst, &tot, sm);
+      C += tot;
     }
-    run += tot;
+    const int Ng = a.wgs_per_head < C ? a.wgs_per_head : C;
+    if (k >= Ng) return;
+    c0 = static_cast<int64_t>(k) * C / Ng;
+    c1 = static_cast<int64_t>(k + 1) * C / Ng;
+    int run = 0;
+    for (int base = 0; base < S; base += kThreads) {
+      if (threadIdx.x == 0) sm.found_seq = -1;
+      const int sq = base + threadIdx.x;
+      const int cst = sq < S ? cost_of(blocks_of(a.context_lens[sq])) : 0;
+      int tot;
+      const int incl = run + block_scan<BF16, D>(cst, &tot, sm);
+      if (sq < S && cst > 0 && incl > c0 && incl - cst <= c0) {
+        sm.found_seq = sq;
+        sm.found_pre = incl - cst;
+      }
+      __syncthreads();
+      const int fs = sm.found_seq;
+      const int fp = sm.found_pre;
+      __syncthreads();
+      if (fs >= 0) {
+        s = fs;
+        pre = fp;
+        break;
+      }
+      run += tot;
+    }
   }
+  const int Ng = a.wgs_per_head < C ? a.wgs_per_head : C;
 
-  // Walk the segments of [b0, b1).
-  for (; s < S && pre < b1; ++s) {
-    const int Lr = a.context_lens[s];
+  // Walk the segments: the sequences whose blocks meet [c0, c1).  Every one
+  // visited holds at least one block of the range (lb0 < lb1).
+  for (; s < S && static_cast<int64_t>(pre) + a.seg_cost < c1; ++s) {
+    const int Lr = small ? __builtin_amdgcn_readfirstlane(sm.lens[s]) : a.context_lens[s];
     const int L = clamp_len(Lr, a.max_context_len);
     const int nb = (L + BS - 1) / BS;
     if (nb == 0) continue;
-    const int lb0 = static_cast<int>((b0 > pre ? b0 : pre) - pre);
-    const int lb1 = static_cast<int>((b1 < static_cast<int64_t>(pre) + nb ? b1 : static_cast<int64_t>(pre) + nb) - pre);
+    const int64_t x0 = static_cast<int64_t>(pre) + a.seg_cost;  // list position of block 0
+    const int lb0 = static_cast<int>((c0 > x0 ? c0 : x0) - x0);
+    const int lb1 = static_cast<int>((c1 < x0 + nb ? c1 : x0 + nb) - x0);
     const bool whole = lb0 == 0 && lb1 == nb;
     const int prow = whole ? -1 : (b * 2 + (lb0 == 0 ? 1 : 0));
     // A length outside [1, max_context_len] appends nothing: a clamped length
     // would name a slot that already holds a cached token.
     decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, appending && lb1 == nb && Lr == L, sm);
     if (lb0 == 0 && threadIdx.x == 0) {
-      // Workgroup (within this head) holding block x of the list: the largest
-      // k' with k' T / Ng <= x.
-      const int64_t last = pre + nb - 1;
-      const int k_last = static_cast<int>(((last + 1) * Ng - 1) / T);
+      // Workgroup (within this head) whose range holds list position x: the
+      // largest k' with k' C / Ng <= x.
+      const int64_t last = x0 + nb - 1;
+      const int k_last = static_cast<int>(((last + 1) * Ng - 1) / C);
       int32_t* mt = a.meta + (static_cast<size_t>(s) * Hkv + g) * 2;
       mt[0] = k;
       mt[1] = k_last - k + 1;
     }
-    pre += nb;
+    pre += nb + a.seg_cost;
   }
 }
 
@@ -963,6 +1003,16 @@ int64_t wgs_per_head_for(int64_t num_seqs, int64_t num_kv_heads, int64_t max_con
   return n;
 }
 
+// Fixed work of one decode segment (block-id staging, query load, the first
+// K/V round trip, the cross-wave merge and its output or partial), as a
+// number of blocks of K/V streaming that take as long; the balanced split
+// charges it per sequence.
+constexpr int kSegmentCostTokens = 128;
+
+int32_t segment_cost_blocks(int32_t block_size) {
+  return static_cast<int32_t>((kSegmentCostTokens + block_size - 1) / block_size);
+}
+
 // Workspace: 256-byte aligned regions
 //   meta int32[S*Hkv*2] | m float[N*2*G] | l float[N*2*G] | acc float[N*2*G*D]
 struct WsLayout {
@@ -1193,6 +1243,12 @@ int32_t paged_attention_workgroups_per_head(int32_t num_seqs, int32_t num_kv_hea
   return static_cast<int32_t>(n);
 }
 
+int32_t paged_attention_segment_cost(int32_t block_size) {
+  if (block_size != 16 && block_size != 32) return pkv::fail(PKV_ERR_UNSUPPORTED, "block_size %d not supported", block_size);
+  pkv::ok();
+  return segment_cost_blocks(block_size);
+}
+
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                        int32_t block_size, int32_t max_context_len, int32_t partition_size) {
   if (check_common(head_dim, block_size, PKV_BF16)) return 0;
@@ -1306,6 +1362,7 @@ int32_t decode_call(void* out, const void* q, const void* k_new, const void* v_n
   a.ws_acc = reinterpret_cast<float*>(ws + wl.acc);
   a.status = status;
   a.wgs_per_head = static_cast<int32_t>(wph);
+  a.seg_cost = segment_cost_blocks(block_size);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;

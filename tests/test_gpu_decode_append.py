@@ -289,11 +289,27 @@ def test_small_workspace_is_rejected_before_any_launch():
     assert torch.equal(k, k0) and torch.equal(v, v0), "a rejected call must not touch the pools"
 
 
-def _ranges(lens, bs, wph):
-    """Blocks [b0, b1) of the per-head block list each decode workgroup takes."""
-    T = sum(-(-L // bs) for L in lens)
-    ng = min(wph, T)
-    return [(k * T // ng, (k + 1) * T // ng) for k in range(ng)]
+def _ranges(lens, bs, wph, seg_cost):
+    """Block ranges [(seq, lb0, lb1), ...] each decode workgroup of a kv head
+    takes: the head's list charges every non-empty sequence seg_cost blocks
+    before its own blocks, and workgroup k takes positions [k C / W, (k+1) C / W)."""
+    nbs = [-(-L // bs) for L in lens]
+    C = sum(n + seg_cost for n in nbs if n > 0)
+    ng = min(wph, C)
+    out = []
+    for k in range(ng):
+        c0, c1 = k * C // ng, (k + 1) * C // ng
+        pre, segs = 0, []
+        for s, n in enumerate(nbs):
+            if n == 0:
+                continue
+            x0 = pre + seg_cost
+            lb0, lb1 = max(c0, x0) - x0, min(c1, x0 + n) - x0
+            if lb0 < lb1:
+                segs.append((s, lb0, lb1))
+            pre += n + seg_cost
+        out.append(segs)
+    return out
 
 
 @pytest.mark.parametrize("bs", [16, 32])
@@ -307,14 +323,13 @@ def test_folded_append_with_several_sequence_ends_per_workgroup(bs):
     lens = [1, 3, 17, 40, 5000]
     Hq, Hkv, d = 64, 8, 128
     S = len(lens)
-    wph = pkv.paged_attention_workgroups_per_head(S, Hkv, d, bs, max(lens))
-    assert S <= wph, "the append must be folded"
-    starts, ends = [], 0
-    for L in lens:
-        starts.append(ends)
-        ends += -(-L // bs)
-    last_blocks = [st + -(-L // bs) - 1 for st, L in zip(starts, lens)]
-    per_wg = [sum(b0 <= x < b1 for x in last_blocks) for b0, b1 in _ranges(lens, bs, wph)]
+    # eight workgroups per kv head, so the first one's range is long enough
+    # to hold the fixed charges and blocks of the four short sequences
+    part = -(-S * max(lens) // 8)
+    wph = pkv.paged_attention_workgroups_per_head(S, Hkv, d, bs, max(lens), part)
+    assert wph == 8 and S <= wph, "the append must be folded"
+    ranges = _ranges(lens, bs, wph, pkv.paged_attention_segment_cost(bs))
+    per_wg = [sum(lb1 == -(-lens[s] // bs) for s, _, lb1 in segs) for segs in ranges]
     say(f"case decode_append several ends per workgroup bs{bs}: up to {max(per_wg)} ends in one workgroup")
     assert max(per_wg) >= 2
     g = torch.Generator().manual_seed(4242 + bs)
@@ -345,10 +360,11 @@ def test_folded_append_with_several_sequence_ends_per_workgroup(bs):
     new_slots = np.array([int(tables[s, (L - 1) // bs]) * bs + (L - 1) % bs for s, L in enumerate(lens)], np.int64)
     outA = torch.empty(S, Hq, d, dtype=torch.bfloat16, device="cuda")
     pkv.paged_kv_append(kn.cuda(), vn.cuda(), kA, vA, torch.from_numpy(new_slots.astype(np.int32)).cuda())
-    pkv.paged_attention_decode(outA, q.cuda(), kA, vA, tab, ln, max(lens))
+    pkv.paged_attention_decode(outA, q.cuda(), kA, vA, tab, ln, max(lens), partition_size=part)
     outB = torch.empty_like(outA)
     pkv.device_status()
-    pkv.paged_attention_decode_append(outB, q.cuda(), kn.cuda(), vn.cuda(), kB, vB, tab, ln, max(lens))
+    pkv.paged_attention_decode_append(outB, q.cuda(), kn.cuda(), vn.cuda(), kB, vB, tab, ln, max(lens),
+                                      partition_size=part)
     assert pkv.device_status() == 0
     torch.cuda.synchronize()
     assert _bits_equal(kA, kB) and _bits_equal(vA, vB), "pools differ from append + decode"
