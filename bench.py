@@ -44,7 +44,7 @@ HOST_LINK_PEAK = 64.0e9  # PCIe 5.0 x16, one direction, bytes/s
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 MFMA_BF16_PEAK = 2.5e15  # MI355X dense bf16 matrix-core flop/s
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_230_amd", "csrc", "pagedkv_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c3_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 PREFILL_SOURCE = os.path.join(ROOT, "paged_kv_cache_230_amd", "csrc", "prefill_kernel.hip")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_c7_traffic.json")
 
@@ -99,9 +99,10 @@ def load_traffic(workload, partition):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_sha() or t.get("workload") != workload or partition != 0:
+    rec = t.get("workloads", {}).get(workload)
+    if t.get("kernel_source_sha256") != kernel_source_sha() or rec is None or partition != 0:
         return None
-    return t.get("hbm_bytes_per_decode_call")
+    return rec.get("hbm_bytes_per_decode_call")
 
 
 def load_prefill_traffic(workload, steps, warmup):
@@ -738,6 +739,9 @@ def main():
                     help="event-timed decode calls for the roofline, and event-bounded steps for the distribution")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--block-size", type=int, default=None, choices=(16, 32),
+                    help="run the workload's batch at this block size instead of its own (for A/B runs; the "
+                         "headline figure uses the workload's block size)")
     ap.add_argument("--aux-paging", action="store_true",
                     help="instead of the benchmark: decode over the shuffled pool vs a contiguous one, and the "
                          "slot waste of paging vs max-length reservation")
@@ -758,7 +762,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = Workload(args.workload)
+    w = Workload(args.workload, overrides={} if args.block_size is None else {"block_size": args.block_size})
     if args.aux_paging:
         print(json.dumps(run_paging_aux(args, w, dev)), flush=True)
         return

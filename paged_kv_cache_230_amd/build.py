@@ -13,6 +13,10 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libpagedkv.so"
+# A/B library whose bf16 decode kernel runs the Q.K and P.V products on the
+# vector ALUs instead of the matrix cores (same loads, split and merge); it
+# exists to measure that choice and is loaded only through PKV_LIB_PATH.
+VALU_AB_LIB_NAME = "libpagedkv_valu_ab.so"
 SOURCES = ["csrc/pagedkv_kernels.hip", "csrc/prefill_kernel.hip", "csrc/swap_kernel.hip", "csrc/measure_kernel.hip",
            "csrc/block_manager.cpp", "csrc/radix.cpp"]
 ARCH = "gfx950"
@@ -25,11 +29,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpagedkv)")
 
 
-def command(out_path: str) -> list[str]:
+def command(out_path: str, defines: tuple[str, ...] = ()) -> list[str]:
     return [
         hipcc(),
         f"--offload-arch={ARCH}",
         "-O3",
+        *[f"-D{d}" for d in defines],
         "-std=c++17",
         "-fPIC",
         "-shared",
@@ -45,10 +50,10 @@ def command(out_path: str) -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    out = os.path.join(HERE, LIB_NAME)
+def build(verbose: bool = False, valu_ab: bool = False) -> str:
+    out = os.path.join(HERE, VALU_AB_LIB_NAME if valu_ab else LIB_NAME)
     tmp = out + ".tmp"
-    cmd = command(tmp)
+    cmd = command(tmp, ("PKV_DECODE_VALU_DOT=1",) if valu_ab else ())
     res = subprocess.run(cmd, cwd=HERE, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     log = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
@@ -61,4 +66,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, valu_ab="--valu-ab" in sys.argv[1:]))

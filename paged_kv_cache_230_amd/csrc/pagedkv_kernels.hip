@@ -45,6 +45,12 @@
 
 #include "pkv_status.h"
 
+// 1 builds the A/B library whose bf16 decode products run on the vector ALUs
+// (decode_segment_valu); the product library is built with 0.
+#ifndef PKV_DECODE_VALU_DOT
+#define PKV_DECODE_VALU_DOT 0
+#endif
+
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -213,6 +219,10 @@ struct DecodeSmem {
   const void* append_src[2];
   int ids[kIdChunk];  // block ids of the current chunk of the segment
   int lens[kThreads];  // raw context lengths, when the batch has at most kThreads sequences
+#if PKV_DECODE_VALU_DOT
+  uint16_t qv[8][D];          // the group's query rows (bf16), zero past G
+  float pv[kWaves][16][8];    // one unit's probabilities, [token][head], per wave
+#endif
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
@@ -303,6 +313,43 @@ __device__ __forceinline__ void append_store(const DecodeArgs& a, const AppendRo
     else
       reinterpret_cast<uint32_t*>(vc)[tile + static_cast<size_t>(t) * BS + o] = r.v;
   }
+}
+
+// The end of a segment: waves w < nw have left their (max, sum,
+// accumulator) in sm.m/l/o; they are combined, and the output rows (prow <
+// 0) or partial row `prow` written.
+template <bool BF16, int D>
+__device__ __forceinline__ void merge_waves(const DecodeArgs& a, DecodeSmem<BF16, D>& sm, int nw, int prow,
+                                            size_t out_row0) {
+  const int G = a.group;
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += kThreads) {
+    const int hh = e / D;
+    const int d = e - hh * D;
+    float M = sm.m[0][hh];
+    for (int ww = 1; ww < nw; ++ww) M = fmaxf(M, sm.m[ww][hh]);
+    float num = 0.f, den = 0.f;
+    for (int ww = 0; ww < nw; ++ww) {
+      const float f = __builtin_amdgcn_exp2f(sm.m[ww][hh] - M);
+      num += f * sm.o[ww][hh][d];
+      den += f * sm.l[ww][hh];
+    }
+    if (prow < 0) {
+      const float o = num / den;
+      if constexpr (BF16)
+        static_cast<uint16_t*>(a.out)[out_row0 + e] = f32_to_bf16_bits(o);
+      else
+        static_cast<float*>(a.out)[out_row0 + e] = o;
+    } else {
+      const size_t r = static_cast<size_t>(prow) * G + hh;
+      a.ws_acc[r * D + d] = num;
+      if (d == 0) {
+        a.ws_m[r] = M;
+        a.ws_l[r] = den;
+      }
+    }
+  }
+  __syncthreads();  // the next segment reuses the LDS
 }
 
 // Blocks [lb0, lb1) of sequence s (length L) for kv head g.  When
@@ -567,36 +614,221 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
       sm.l[w][row] = l_run;
     }
   }
-  __syncthreads();
+  merge_waves<BF16, D>(a, sm, nw, prow, out_row0);
+}
 
-  for (int e = threadIdx.x; e < G * D; e += kThreads) {
+#if PKV_DECODE_VALU_DOT
+// Vector-ALU variant of the bf16 segment, built only into the A/B library
+// that measures what the matrix cores buy (the product library always uses
+// decode_segment).  Same loads, unit walk, online softmax and merge; the
+// products run on the VALU:
+//   * Q.K: lane (row, quad) holds 32 dims of token `row` (as loaded for the
+//     MFMA); it takes the same dims of each of the GV query heads from LDS
+//     and accumulates v_dot2_f32_bf16 (two bf16 products per instruction)
+//     in two chains, then the four quads' partial dots are summed by
+//     shuffles: every lane ends with the scores of its token for all heads.
+//   * P.V: each wave writes its unit's probabilities to LDS; lane (row,
+//     quad) reads those of tokens 4 quad .. 4 quad + 3 and accumulates, in
+//     fp32 FMAs, dims 16 nt + row of all GV heads over its four tokens; the
+//     quads' partial sums are added at the end of the segment.
+// GV (4 or 8) is the compile-time head count the loops run over.
+template <int D, int BS, int GV>
+__device__ void decode_segment_valu(const DecodeArgs& a, int s, int g, int L, int lb0, int lb1, int prow,
+                                    bool append, DecodeSmem<true, D>& sm) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  constexpr int NT = D / 16;
+  constexpr int KK = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & 15;
+  const int quad = lane >> 4;
+  const int G = a.group;
+  const int Hq = a.num_q_heads;
+  const int start = lb0 * BS;
+  const int end = min(lb1 * BS, L);
+  const int nblk = lb1 - lb0;
+  const int32_t* tbl = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq + lb0;
+  const size_t out_row0 = (static_cast<size_t>(s) * Hq + static_cast<size_t>(g) * G) * D;
+
+  // the group's query rows into LDS (ordered before use by the barrier
+  // after the block-id staging)
+  for (int e = threadIdx.x; e < GV * D; e += kThreads) {
     const int hh = e / D;
-    const int d = e - hh * D;
-    float M = sm.m[0][hh];
-    for (int ww = 1; ww < nw; ++ww) M = fmaxf(M, sm.m[ww][hh]);
-    float num = 0.f, den = 0.f;
-    for (int ww = 0; ww < nw; ++ww) {
-      const float f = __builtin_amdgcn_exp2f(sm.m[ww][hh] - M);
-      num += f * sm.o[ww][hh][d];
-      den += f * sm.l[ww][hh];
+    sm.qv[hh][e - hh * D] = hh < G ? static_cast<const uint16_t*>(a.q)[out_row0 + e] : uint16_t{0};
+  }
+
+  const size_t tile_elems = static_cast<size_t>(D) * BS;
+  const size_t head_off = static_cast<size_t>(g) * tile_elems;
+  const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * tile_elems;
+  const char* kbase = static_cast<const char*>(a.k_cache);
+  const char* vbase = static_cast<const char*>(a.v_cache);
+  auto tile_ptrs = [&](int c, const void*& kt, const void*& vt) {
+    const int b = __builtin_amdgcn_readfirstlane(sm.ids[c]);
+    const size_t off = (static_cast<size_t>(b) * block_stride + head_off) * 2;
+    kt = kbase + off;
+    vt = vbase + off;
+  };
+
+  float acc[NT][GV];
+  float m_run[GV], l_run[GV];
+#pragma unroll
+  for (int h = 0; h < GV; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt][h] = 0.f;
+  }
+
+  auto compute_step = [&](Step<true, D>& st, const int tok_base) {
+    float x[GV];
+    const bool valid = tok_base + row < end;
+#pragma unroll
+    for (int h = 0; h < GV; ++h) {
+      float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint4 qq = *reinterpret_cast<const uint4*>(&sm.qv[h][8 * (4 * kk + quad)]);
+        const uint4 kv = st.k[kk];
+        c0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kv.x), __builtin_bit_cast(bf16x2, qq.x), c0,
+                                             false);
+        c1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kv.y), __builtin_bit_cast(bf16x2, qq.y), c1,
+                                             false);
+        c0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kv.z), __builtin_bit_cast(bf16x2, qq.z), c0,
+                                             false);
+        c1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kv.w), __builtin_bit_cast(bf16x2, qq.w), c1,
+                                             false);
+      }
+      float t = c0 + c1;
+      t += shfl_xor_f(t, 16);
+      t += shfl_xor_f(t, 32);
+      x[h] = valid ? t * a.scale_log2 : -INFINITY;
     }
-    if (prow < 0) {
-      const float o = num / den;
-      if constexpr (BF16)
-        static_cast<uint16_t*>(a.out)[out_row0 + e] = f32_to_bf16_bits(o);
-      else
-        static_cast<float*>(a.out)[out_row0 + e] = o;
-    } else {
-      const size_t r = static_cast<size_t>(prow) * G + hh;
-      a.ws_acc[r * D + d] = num;
-      if (d == 0) {
-        a.ws_m[r] = M;
-        a.ws_l[r] = den;
+    if (tok_base + 16 > end) mask_v<true, D>(st, tok_base + 4 * quad, end);
+    float p[GV], alpha[GV];
+    bool grow = false;
+#pragma unroll
+    for (int h = 0; h < GV; ++h) {
+      float bm = x[h];
+      bm = fmaxf(bm, shfl_xor_f(bm, 1));
+      bm = fmaxf(bm, shfl_xor_f(bm, 2));
+      bm = fmaxf(bm, shfl_xor_f(bm, 4));
+      bm = fmaxf(bm, shfl_xor_f(bm, 8));
+      const float m_new = fmaxf(m_run[h], bm);
+      alpha[h] = __builtin_amdgcn_exp2f(m_run[h] - m_new);
+      grow |= m_new > m_run[h];
+      p[h] = valid ? __builtin_amdgcn_exp2f(x[h] - m_new) : 0.f;
+      l_run[h] = l_run[h] * alpha[h] + p[h];
+      m_run[h] = m_new;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int h = 0; h < GV; ++h) acc[nt][h] *= alpha[h];
+    }
+    if (quad == 0) {
+#pragma unroll
+      for (int h = 0; h < GV; ++h) sm.pv[w][row][h] = p[h];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float pt[4][GV];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < GV; ++h) pt[i][h] = sm.pv[w][4 * quad + i][h];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float v0 = bf16_bits_to_f32(static_cast<uint16_t>(st.v[nt].x & 0xFFFFu));
+      const float v1 = bf16_bits_to_f32(static_cast<uint16_t>(st.v[nt].x >> 16));
+      const float v2 = bf16_bits_to_f32(static_cast<uint16_t>(st.v[nt].y & 0xFFFFu));
+      const float v3 = bf16_bits_to_f32(static_cast<uint16_t>(st.v[nt].y >> 16));
+#pragma unroll
+      for (int h = 0; h < GV; ++h)
+        acc[nt][h] = fmaf(pt[3][h], v3, fmaf(pt[2][h], v2, fmaf(pt[1][h], v1, fmaf(pt[0][h], v0, acc[nt][h]))));
+    }
+    // the next unit's stores to sm.pv come after every lane's reads above
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  constexpr int HALVES = BS / 16;
+  const int h = w % HALVES;
+  const int nunits = (end - start + 15) / 16;
+  auto stage_ids = [&](int c0) {
+    const int cn = nblk - c0 < kIdChunk ? nblk - c0 : kIdChunk;
+    for (int i = threadIdx.x; i < cn; i += kThreads) {
+      const int b = tbl[c0 + i];
+      const bool ok = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks);
+      if (!ok) report(a.status, PKV_DEV_BAD_BLOCK_ID);
+      sm.ids[i] = ok ? b : 0;
+    }
+  };
+  if (append) {
+    const AppendRow<true, D> arow = append_load<true, D, BS>(a, sm.append_src[0], sm.append_src[1], s, g, L);
+    stage_ids(0);
+    append_store<true, D, BS>(a, arow, g, L);
+  } else {
+    stage_ids(0);
+  }
+  for (int c0 = 0; c0 < nblk; c0 += kIdChunk) {
+    const int cn = nblk - c0 < kIdChunk ? nblk - c0 : kIdChunk;
+    if (c0 > 0) stage_ids(c0);
+    __syncthreads();
+    const int uend = c0 * HALVES + (min(start + (c0 + cn) * BS, end) - (start + c0 * BS) + 15) / 16;
+    Step<true, D> st, nxt;
+    const void* kt = nullptr;
+    const void* vt = nullptr;
+    int u = c0 * HALVES + w;
+    if (u < uend) {
+      tile_ptrs(u / HALVES - c0, kt, vt);
+      load_step<true, D, BS>(st, kt, vt, h, row, quad);
+      for (;;) {
+        const int un = u + kWaves;
+        if (un >= uend) break;
+        tile_ptrs(un / HALVES - c0, kt, vt);
+        load_step<true, D, BS>(nxt, kt, vt, h, row, quad);
+        compute_step(st, start + 16 * u);
+        st = nxt;
+        u = un;
+      }
+      compute_step(st, start + 16 * u);
+    }
+    __syncthreads();
+  }
+
+  // per-wave totals: l over the 16 token rows, accumulators over the quads
+#pragma unroll
+  for (int hh = 0; hh < GV; ++hh) {
+    float t = l_run[hh];
+    t += shfl_xor_f(t, 1);
+    t += shfl_xor_f(t, 2);
+    t += shfl_xor_f(t, 4);
+    t += shfl_xor_f(t, 8);
+    l_run[hh] = t;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      acc[nt][hh] += shfl_xor_f(acc[nt][hh], 16);
+      acc[nt][hh] += shfl_xor_f(acc[nt][hh], 32);
+    }
+  }
+  const int nw = nunits < kWaves ? nunits : kWaves;
+  if (w < nw && quad == 0) {
+#pragma unroll
+    for (int hh = 0; hh < GV; ++hh) {
+      if (hh < G) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sm.o[w][hh][16 * nt + row] = acc[nt][hh];
+        if (row == 0) {
+          sm.m[w][hh] = m_run[hh];
+          sm.l[w][hh] = l_run[hh];
+        }
       }
     }
   }
-  __syncthreads();  // the next segment reuses the LDS
+  merge_waves<true, D>(a, sm, nw, prow, out_row0);
 }
+#endif
 
 // Balanced split.  For one kv head, the blocks of all sequences form one
 // list (sequence after sequence) in which every non-empty sequence is also
@@ -609,19 +841,29 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
 // (one per sequence touched): a segment that is a whole sequence writes its
 // output rows; a piece of a split sequence writes a partial, and the
 // workgroup holding the sequence's first block records (first workgroup,
-// number of pieces) for the merge kernel.  With 8 kv heads the round-robin
-// dealing of workgroups to the 8 XCDs gives each XCD one head.
-// Minimum waves per SIMD the compiler must leave room for: 3 for bf16 (142
-// VGPRs at head_dim 128, no spills); fp32 keeps its natural allocation.
+// number of pieces) for the merge kernel.
+// Minimum waves per SIMD the compiler must leave room for: 3 for bf16 (about
+// 154 VGPRs at head_dim 128, no spills); fp32 keeps its natural allocation.
+// The VALU variant holds 8 dims x 8 heads of fp32 accumulators per lane and
+// fits in 2 without spills.
 template <bool BF16>
-constexpr int kDecodeMinWaves = BF16 ? 3 : 1;
+constexpr int kDecodeMinWaves = BF16 ? (PKV_DECODE_VALU_DOT ? 2 : 3) : 1;
 
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<BF16, D> sm;
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
-  const int b = blockIdx.x;
+  // Workgroup b = k * Hkv + g serves piece k of kv head g.  The hardware
+  // deals consecutive workgroup ids round robin to the 8 XCDs; at block size
+  // 16 the ids are dealt so that each XCD runs a contiguous run of b, i.e.
+  // every head's pieces (c3 0.3802 vs 0.3833 ms, c2 0.1204 vs 0.1225 ms per
+  // step against one head per XCD); at block size 32 one head per XCD
+  // measured 1 % faster and is kept.
+  const int n_wg = static_cast<int>(gridDim.x);
+  const int b = (BS == 16 && n_wg % 8 == 0)
+                    ? static_cast<int>(blockIdx.x % 8) * (n_wg / 8) + static_cast<int>(blockIdx.x / 8)
+                    : static_cast<int>(blockIdx.x);
   const int g = b % Hkv;
   const int k = b / Hkv;
   const bool appending = a.k_new != nullptr;
@@ -721,7 +963,16 @@ __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel
     const int prow = whole ? -1 : (b * 2 + (lb0 == 0 ? 1 : 0));
     // A length outside [1, max_context_len] appends nothing: a clamped length
     // would name a slot that already holds a cached token.
-    decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, appending && lb1 == nb && Lr == L, sm);
+    const bool app = appending && lb1 == nb && Lr == L;
+#if PKV_DECODE_VALU_DOT
+    if constexpr (BF16) {
+      if (a.group <= 4)
+        decode_segment_valu<D, BS, 4>(a, s, g, L, lb0, lb1, prow, app, sm);
+      else
+        decode_segment_valu<D, BS, 8>(a, s, g, L, lb0, lb1, prow, app, sm);
+    } else
+#endif
+      decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, app, sm);
     if (lb0 == 0 && threadIdx.x == 0) {
       // Workgroup (within this head) whose range holds list position x: the
       // largest k' with k' C / Ng <= x.
