@@ -25,6 +25,7 @@ timed on the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -44,6 +45,7 @@ HOST_LINK_PEAK = 64.0e9  # PCIe 5.0 x16, one direction, bytes/s
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 MFMA_BF16_PEAK = 2.5e15  # MI355X dense bf16 matrix-core flop/s
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_230_amd", "csrc", "pagedkv_kernels.hip")
+DEFAULT_STEPS = {"c3_70b_32k_bf16": (200, 20), "c2_8b_bf16": (200, 20)}  # (timed, warm-up); others (30, 5)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 PREFILL_SOURCE = os.path.join(ROOT, "paged_kv_cache_230_amd", "csrc", "prefill_kernel.hip")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_c7_traffic.json")
@@ -563,7 +565,8 @@ def run_multiturn(args, w, dev):
         out = torch.empty_like(qs[t])
         tables, lens, _, lh = cache.tables(sids)
         ev[t][0].record()
-        pkv.paged_attention_decode(out, qs[t], cache.k_cache, cache.v_cache, tables, lens, int(lh.max()))
+        pkv.paged_attention_decode(out, qs[t], cache.k_cache, cache.v_cache, tables, lens, int(lh.max()),
+                                   shared_blocks=cache.bm.num_shared() > 0)
         ev[t][1].record()
         kv_bytes.append(decode_kv_bytes(lh, c.num_kv_heads, c.head_dim, c.elem_bytes))
         for i, sid in enumerate(sids):
@@ -680,9 +683,11 @@ def run_paging_aux(args, w, dev):
                                                                  max_len, args.partition), 256),
                          dtype=torch.uint8, device=dev)
 
+        shared = cache.bm.num_shared() > 0 if args.shared_blocks == "auto" else args.shared_blocks == "on"
+
         def call():
             pkv.paged_attention_decode(out, q, cache.k_cache, cache.v_cache, tab_d, lens_d, max_len,
-                                       partition_size=args.partition, workspace=ws)
+                                       partition_size=args.partition, workspace=ws, shared_blocks=shared)
 
         for _ in range(args.warmup):
             call()
@@ -721,8 +726,10 @@ def run_paging_aux(args, w, dev):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 200 for the 32k layer and the 8B-shaped batch, 30 for the others)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: 20 for the 32k layer and the 8B-shaped batch, 5 for the others)")
     ap.add_argument("--workload", default="c3_70b_32k_bf16")
     ap.add_argument("--partition", type=int, default=0,
                     help="about this many tokens per decode workgroup (0 = one round of resident workgroups)")
@@ -742,6 +749,9 @@ def main():
     ap.add_argument("--block-size", type=int, default=None, choices=(16, 32),
                     help="run the workload's batch at this block size instead of its own (for A/B runs; the "
                          "headline figure uses the workload's block size)")
+    ap.add_argument("--shared-blocks", choices=("auto", "on", "off"), default="auto",
+                    help="decode cache policy: auto sets PKV_DECODE_SHARED_BLOCKS when the block manager holds "
+                         "shared blocks; on / off force it (results are identical, only the time differs)")
     ap.add_argument("--aux-paging", action="store_true",
                     help="instead of the benchmark: decode over the shuffled pool vs a contiguous one, and the "
                          "slot waste of paging vs max-length reservation")
@@ -763,6 +773,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = Workload(args.workload, overrides={} if args.block_size is None else {"block_size": args.block_size})
+    # The 32k layer's step is 0.34 ms and the 8B-shaped batch's 0.11 ms: 200
+    # timed steps keep a single host hiccup or the pipeline's start from
+    # moving the mean, and 20 warm-up steps let a fresh process's host path
+    # settle (a first run on a fresh box has issued steps at 3x the host time
+    # of the next).  The other workloads keep 30 / 5: their pools are sized
+    # for the lengths they reach in that many steps.
+    d_steps, d_warmup = DEFAULT_STEPS.get(w.name, (30, 5))
+    args.steps = d_steps if args.steps is None else args.steps
+    args.warmup = d_warmup if args.warmup is None else args.warmup
     if args.aux_paging:
         print(json.dumps(run_paging_aux(args, w, dev)), flush=True)
         return
@@ -812,6 +831,9 @@ def main():
     step_ids = [w.step_tokens(k) for k in range(nsteps)]  # None unless the workload tracks token ids
     bm = cache.bm
     seqs = np.asarray(w.decode_seqs, np.int64)
+    # Cache policy of the decode calls: read K/V through the caches when the
+    # batch's sequences share blocks (prefix sharing, forks), else stream them.
+    shared_blocks = bm.num_shared() > 0 if args.shared_blocks == "auto" else args.shared_blocks == "on"
     bs = c.block_size
     max_len_bound = int(max(bm.seq_len(int(s)) for s in seqs)) + nsteps
     max_blocks = -(-max_len_bound // bs)
@@ -876,10 +898,11 @@ def main():
             ev0[k].record()
         if args.separate_append:
             pkv.paged_attention_decode(out, step_q[k], cache.k_cache, cache.v_cache, tables_d, lens_d, max_len,
-                                       partition_size=P, workspace=workspace)
+                                       partition_size=P, workspace=workspace, shared_blocks=shared_blocks)
         else:
             pkv.paged_attention_decode_append(out, step_q[k], step_k[k], step_v[k], cache.k_cache, cache.v_cache,
-                                              tables_d, lens_d, max_len, partition_size=P, workspace=workspace)
+                                              tables_d, lens_d, max_len, partition_size=P, workspace=workspace,
+                                              shared_blocks=shared_blocks)
         if k in marked or k in dist:
             ev1[k].record()
         if nsets > 1:
@@ -898,11 +921,14 @@ def main():
         step(k)
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    gc.collect()
+    gc.disable()  # no collector pause inside the timed steps
     t0 = time.perf_counter()
     for k in range(args.warmup, args.warmup + args.steps):
         step(k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     for k in marked:
         step(k)
     for k in dist:
@@ -978,6 +1004,7 @@ def main():
         # the single call writes the step's rows from inside the decode kernel
         # when there is at most one sequence per decode workgroup of a kv head
         "append_folded": (not args.separate_append) and S <= wph,
+        "shared_blocks": shared_blocks,
         "host_us_per_step": round(1e6 * sum(host_s[k] for k in timed) / args.steps, 1),
         # step k+1's bookkeeping staged on a second stream during step k's decode
         "stage_overlapped": nsets > 1,

@@ -86,6 +86,20 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 #define PKV_DEV_BAD_RECORD 16     /* a staged table update outside the device table     */
 #define PKV_DEV_BAD_QUERY_START 32 /* prefill query_start not rising in [0, num_tokens] */
 
+/* Flags of the decode calls (paged_attention_decode*).                    */
+/* PKV_DECODE_SHARED_BLOCKS: several sequences of the batch read the same  */
+/*   blocks (shared prompt prefixes, forked samples: "PagedAttention et    */
+/*   RadixAttention : parlons de KV Cache", step 4, and the part on        */
+/*   automatic prefix caching).  The kernel then reads K/V through the     */
+/*   caches and keeps each kv head's workgroups on one XCD, so a shared    */
+/*   block fetched for one sequence serves the others from that XCD's L2.  */
+/*   Without the flag, K/V are streamed with non-temporal loads, which do  */
+/*   not fill the caches: faster when every block is read once per call.   */
+/*   Results are identical either way; the flag only chooses the faster     */
+/*   schedule.  pkv_bm_num_shared tells whether a block manager's pool     */
+/*   holds shared blocks.                                                  */
+#define PKV_DECODE_SHARED_BLOCKS 1u
+
 /* Message for the last failing call on this thread ("" if none).  The
  * string is owned by the library and valid until the thread's next call. */
 const char* pkv_last_error(void);
@@ -198,18 +212,21 @@ int32_t paged_kv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, 
 /*                 content is accepted (each call writes what it reads);  */
 /*                 calls sharing a workspace must be ordered on one       */
 /*                 stream.                                                */
+/* flags         : 0 or PKV_DECODE_SHARED_BLOCKS (cache policy, above);   */
+/*                 other bits fail with PKV_ERR_INVALID_ARG               */
 /*                                                                        */
 /* Work distribution (balanced split): for each kv head the blocks of all */
-/* sequences form one list of T blocks; each of the N workgroups of that  */
-/* head takes an equal contiguous range of it.  A range covering a whole  */
-/* sequence writes its rows; pieces of a split sequence write partials    */
-/* that a second kernel merges by log-sum-exp.                            */
+/* sequences form one list in which every sequence is also charged       */
+/* paged_attention_segment_cost(block_size) blocks of fixed work; each of */
+/* the N workgroups of that head takes an equal contiguous range of it.   */
+/* A range covering a whole sequence writes its rows; pieces of a split   */
+/* sequence write partials that a second kernel merges by log-sum-exp.    */
 int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                                float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
-                               pkv_dtype dt, void* stream);
+                               pkv_dtype dt, uint32_t flags, void* stream);
 
 /* Decode attention with the step's cache append folded in ([aitalk]     */
 /* step 3: each new token's K/V goes into the next slot of the sequence's */
@@ -242,7 +259,7 @@ int32_t paged_attention_decode_append(void* out, const void* q, const void* k_ne
                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                       int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                                       float scale, int32_t partition_size, void* workspace,
-                                      size_t workspace_bytes, pkv_dtype dt, void* stream);
+                                      size_t workspace_bytes, pkv_dtype dt, uint32_t flags, void* stream);
 
 /* paged_attention_decode_append without a caller workspace, for callers */
 /* that cannot allocate device memory (code under HIP graph capture,      */
@@ -263,7 +280,7 @@ int32_t paged_attention_decode_append_noalloc(void* out, const void* q, const vo
                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                               int32_t num_blocks, int32_t max_blocks_per_seq,
                                               int32_t max_context_len, float scale, int32_t partition_size,
-                                              pkv_dtype dt, void* stream);
+                                              pkv_dtype dt, uint32_t flags, void* stream);
 
 /* Workgroups per kv head that paged_attention_decode uses for these     */
 /* arguments on the current device, or a negative status.                 */
@@ -515,6 +532,10 @@ int32_t pkv_bm_stage_capacity(int32_t n_seqs, int32_t max_blocks_per_seq);
 /* Queries.  Negative status on a bad handle or id.                        */
 int32_t pkv_bm_num_free(const pkv_block_manager* bm);
 int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);
+/* Blocks of the device pool held by more than one sequence right now     */
+/* (refcount >= 2), kept up to date by every call that changes a          */
+/* refcount; a nonzero count is the hint for PKV_DECODE_SHARED_BLOCKS.    */
+int32_t pkv_bm_num_shared(const pkv_block_manager* bm);
 int32_t pkv_bm_seq_len(const pkv_block_manager* bm, int64_t seq_id);
 int32_t pkv_bm_num_seqs(const pkv_block_manager* bm);
 /* Free pool, bottom to top (the next block handed out is last);          */

@@ -37,6 +37,7 @@ PKV_DEV_BAD_SLOT = 4
 PKV_DEV_BAD_PAIR = 8
 PKV_DEV_BAD_RECORD = 16
 PKV_DEV_BAD_QUERY_START = 32
+PKV_DECODE_SHARED_BLOCKS = 1  # decode flag: several sequences read the same blocks
 
 STATUS_NAMES = {
     PKV_ERR_INVALID_ARG: "INVALID_ARG",
@@ -63,6 +64,7 @@ if not os.path.exists(LIB_PATH):
 lib = C.CDLL(LIB_PATH)
 
 _i32, _i64, _sz, _f32, _vp = C.c_int32, C.c_int64, C.c_size_t, C.c_float, C.c_void_p
+_u32 = C.c_uint32
 _pi32 = C.POINTER(C.c_int32)
 _pi64 = C.POINTER(C.c_int64)
 _u64 = C.c_uint64
@@ -78,17 +80,17 @@ _SIGS = {
     "paged_attention_decode": (
         _i32,
         [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32,
-         _vp],
+         _u32, _vp],
     ),
     "paged_attention_decode_append": (
         _i32,
         [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
-         _sz, _i32, _vp],
+         _sz, _i32, _u32, _vp],
     ),
     "paged_attention_decode_append_noalloc": (
         _i32,
         [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
-         _vp],
+         _u32, _vp],
     ),
     "paged_attention_workgroups_per_head": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attention_segment_cost": (_i32, [_i32]),
@@ -105,6 +107,7 @@ _SIGS = {
     "pkv_bm_block_tables": (_i32, [_vp, _pi64, _i32, _i32, _pi32, _pi32]),
     "pkv_bm_num_free": (_i32, [_vp]),
     "pkv_bm_refcount": (_i32, [_vp, _i32]),
+    "pkv_bm_num_shared": (_i32, [_vp]),
     "pkv_bm_seq_len": (_i32, [_vp, _i64]),
     "pkv_bm_num_seqs": (_i32, [_vp]),
     "pkv_bm_free_stack": (_i32, [_vp, _pi32, _i32]),

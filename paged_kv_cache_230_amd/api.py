@@ -174,12 +174,15 @@ def paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_di
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,
-                           partition_size=0, workspace=None):
+                           partition_size=0, workspace=None, shared_blocks=False):
     """Decode attention; writes ``out`` ([S][H_q][d], dtype of q) and returns it.
 
     ``workspace`` is a uint8 device tensor of at least
     ``paged_attention_workspace_bytes(...)`` bytes; allocated with torch
-    when omitted.
+    when omitted.  ``shared_blocks``: several sequences read the same blocks
+    (shared prefixes, forks), so K/V are read through the caches instead of
+    streamed (``PKV_DECODE_SHARED_BLOCKS``); the result is the same either
+    way.
     """
     nb, H, d, bs = _pool_dims(k_cache, v_cache)
     dev = k_cache.device
@@ -205,14 +208,19 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         N.lib.paged_attention_decode(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, Hq, H, d,
             bs, nb, block_tables.shape[1], int(max_context_len), float(scale), int(partition_size), _ptr(workspace),
-            workspace.numel() if workspace is not None else 0, _dt(k_cache.dtype), _stream(dev),
+            workspace.numel() if workspace is not None else 0, _dt(k_cache.dtype), _flags(shared_blocks),
+            _stream(dev),
         )
     )
     return out
 
 
+def _flags(shared_blocks):
+    return N.PKV_DECODE_SHARED_BLOCKS if shared_blocks else 0
+
+
 def paged_attention_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
-                                  max_context_len, scale=None, partition_size=0, workspace=None):
+                                  max_context_len, scale=None, partition_size=0, workspace=None, shared_blocks=False):
     """Append each sequence's new token (position ``context_lens[s] - 1``)
     from ``k_new``/``v_new`` ([S][H_kv][d]) into its slot, then decode
     attention as :func:`paged_attention_decode`; one call, one launch fewer."""
@@ -245,14 +253,14 @@ def paged_attention_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_
             _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
             _ptr(context_lens), S, Hq, H, d, bs, nb, block_tables.shape[1], int(max_context_len), float(scale),
             int(partition_size), _ptr(workspace), workspace.numel() if workspace is not None else 0,
-            _dt(k_cache.dtype), _stream(dev),
+            _dt(k_cache.dtype), _flags(shared_blocks), _stream(dev),
         )
     )
     return out
 
 
 def paged_attention_decode_append_noalloc(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
-                                          max_context_len, scale=None, partition_size=0):
+                                          max_context_len, scale=None, partition_size=0, shared_blocks=False):
     """:func:`paged_attention_decode_append` with the library's built-in
     scratch instead of a workspace: the call allocates no device memory."""
     nb, H, d, bs = _pool_dims(k_cache, v_cache)
@@ -276,7 +284,7 @@ def paged_attention_decode_append_noalloc(out, q, k_new, v_new, k_cache, v_cache
         N.lib.paged_attention_decode_append_noalloc(
             _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
             _ptr(context_lens), S, Hq, H, d, bs, nb, block_tables.shape[1], int(max_context_len), float(scale),
-            int(partition_size), _dt(k_cache.dtype), _stream(dev),
+            int(partition_size), _dt(k_cache.dtype), _flags(shared_blocks), _stream(dev),
         )
     )
     return out
@@ -562,6 +570,10 @@ class BlockManager:
 
     def refcount(self, block: int) -> int:
         return N.check(N.lib.pkv_bm_refcount(self._h, int(block)))
+
+    def num_shared(self) -> int:
+        """Device blocks held by more than one sequence (the hint for ``shared_blocks``)."""
+        return N.check(N.lib.pkv_bm_num_shared(self._h))
 
     def seq_len(self, seq_id: int) -> int:
         return N.check(N.lib.pkv_bm_seq_len(self._h, int(seq_id)))

@@ -100,4 +100,4 @@ class PagedKVCache:
             out = torch.empty_like(q)
         max_len = int(lh.max(initial=0))
         return paged_attention_decode(out, q, self.k_cache, self.v_cache, tables, lens, max_len, scale=scale,
-                                      partition_size=partition_size)
+                                      partition_size=partition_size, shared_blocks=self.bm.num_shared() > 0)

@@ -83,6 +83,7 @@ struct pkv_block_manager {
   int32_t block_size = 0;
   std::vector<int32_t> free_stack;  // back() is handed out next
   std::vector<int32_t> refcount;
+  int32_t num_shared = 0;  // blocks with refcount >= 2
   std::unordered_map<int64_t, Seq> seqs;
   // Prefix cache: digest registry, each block's digest, and the eviction
   // list of registered blocks at refcount 0 (a doubly linked list over block
@@ -174,12 +175,21 @@ void complete_block(BM* bm, BM::Seq& s, int32_t i) {
   }
 }
 
+// Refcount changes that keep num_shared (blocks held at least twice) exact.
+inline void ref_inc(BM* bm, int32_t b) {
+  if (++bm->refcount[b] == 2) ++bm->num_shared;
+}
+inline int32_t ref_dec(BM* bm, int32_t b) {
+  if (bm->refcount[b]-- == 2) --bm->num_shared;
+  return bm->refcount[b];
+}
+
 // Drops one reference from each block of a table: blocks reaching zero go
 // to the free stack in logical order, registered ones to the eviction list
 // from the last to the first.
 void release_table(BM* bm, const std::vector<int32_t>& t) {
   for (int32_t b : t) {
-    if (--bm->refcount[b] == 0 && !bm->registered[b]) bm->free_stack.push_back(b);
+    if (ref_dec(bm, b) == 0 && !bm->registered[b]) bm->free_stack.push_back(b);
   }
   for (auto r = t.rbegin(); r != t.rend(); ++r) {
     if (bm->refcount[*r] == 0 && bm->registered[*r]) lru_push_back(bm, *r);
@@ -258,7 +268,7 @@ int32_t pkv_bm_add_seq_cached(pkv_block_manager* bm, int64_t seq_id, const int32
   match_prefix(bm, tokens, n_tokens, salt, &s.table, &s.digests);
   for (int32_t b : s.table) {
     if (bm->refcount[b] == 0) lru_remove(bm, b);
-    bm->refcount[b] += 1;
+    ref_inc(bm, b);
   }
   s.len = static_cast<int32_t>(s.table.size()) * bm->block_size;
   s.salt = salt;
@@ -313,7 +323,7 @@ int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child, int32_
   s.tokens.assign(ps.tokens.begin(), ps.tokens.begin() + std::min<size_t>(num_tokens, ps.tokens.size()));
   s.digests.assign(ps.digests.begin(),
                    ps.digests.begin() + std::min<size_t>(num_tokens / bm->block_size, ps.digests.size()));
-  for (int32_t b : s.table) bm->refcount[b] += 1;
+  for (int32_t b : s.table) ref_inc(bm, b);
   bm->seqs.emplace(child, std::move(s));
   return pkv::ok();
 }
@@ -394,7 +404,7 @@ int32_t pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32
           cow_pairs_out[2 * nc] = old;
           cow_pairs_out[2 * nc + 1] = b;
           ++nc;
-          if (--bm->refcount[old] == 0) released.push_back(old);  // registered; last holder gone
+          if (ref_dec(bm, old) == 0) released.push_back(old);  // registered; last holder gone
           bm->refcount[b] = 1;
           s.table[L / bs] = b;
           for (int32_t& d : s.dirty_from)
@@ -480,6 +490,12 @@ int32_t pkv_bm_cached_digest(const pkv_block_manager* bm, int32_t block, uint8_t
   if (!out) return pkv::fail(PKV_ERR_INVALID_ARG, "out is null");
   std::copy(bm->block_digest[block].begin(), bm->block_digest[block].end(), out);
   return 1;
+}
+
+int32_t pkv_bm_num_shared(const pkv_block_manager* bm) {
+  if (int32_t e = check_handle(bm)) return e;
+  pkv::ok();
+  return bm->num_shared;
 }
 
 int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block) {

@@ -56,6 +56,10 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short short4v;
 typedef __attribute__((ext_vector_type(4))) float float4v;
+// plain vector types for the non-temporal load builtin
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4v;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2v;
+typedef __attribute__((ext_vector_type(4))) float f32x4v;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -141,27 +145,58 @@ struct Step<false, D> {
 };
 
 // Issue the loads of half `h` (16 tokens) of a block tile.
-template <bool BF16, int D, int BS>
+//
+// Cache policy (SH: the call's flags say that several sequences read the
+// same blocks).  Without sharing, each K/V byte is read once per call, so
+// the loads are non-temporal (the `nt` policy): a plain load also
+// allocates each streamed line in the 256 MB Infinity Cache, and with
+// gigabytes streaming through that costs bandwidth (the 16 x 32k layer's
+// decode call took 335 instead of 374 us).  The exception is V at block
+// size 32: one dimension's V row is 64 bytes, a 16-token unit reads half of
+// it and the partner wave reads the other half, which then has to be found
+// in cache; there V loads are plain (with non-temporal V the mixed-length
+// bs32 batch was 10 % slower, with plain V and non-temporal K 6 % faster
+// than all plain).  With sharing (prefix caching, forked samples) a block
+// fetched for one sequence should serve the others from cache, so every
+// load is plain (the 400 forked samples of 50 prompts: 234 against 285 us).
+template <typename T, typename V>
+__device__ __forceinline__ T load_nt(const T* p) {
+  return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const V*>(p)));
+}
+
+template <bool BF16, int D, int BS, bool SH>
 __device__ __forceinline__ void load_step(Step<BF16, D>& st, const void* k_tile, const void* v_tile, int h, int row,
                                           int quad) {
+  constexpr bool kKnt = !SH;
+  constexpr bool kVnt = !SH && BS == 16;  // a unit reads whole V rows
   if constexpr (BF16) {
     const uint16_t* kt = static_cast<const uint16_t*>(k_tile);
     const uint16_t* vt = static_cast<const uint16_t*>(v_tile);
 #pragma unroll
     for (int kk = 0; kk < Step<BF16, D>::KK; ++kk)
-      st.k[kk] = *reinterpret_cast<const uint4*>(kt + ((4 * kk + quad) * BS + 16 * h + row) * 8);
+    {
+      const uint4* p = reinterpret_cast<const uint4*>(kt + ((4 * kk + quad) * BS + 16 * h + row) * 8);
+      st.k[kk] = kKnt ? load_nt<uint4, u32x4v>(p) : *p;
+    }
 #pragma unroll
-    for (int nt = 0; nt < Step<BF16, D>::NT; ++nt)
-      st.v[nt] = *reinterpret_cast<const uint2*>(vt + (16 * nt + row) * BS + 16 * h + 4 * quad);
+    for (int nt = 0; nt < Step<BF16, D>::NT; ++nt) {
+      const uint2* p = reinterpret_cast<const uint2*>(vt + (16 * nt + row) * BS + 16 * h + 4 * quad);
+      st.v[nt] = kVnt ? load_nt<uint2, u32x2v>(p) : *p;
+    }
   } else {
     const float* kt = static_cast<const float*>(k_tile);
     const float* vt = static_cast<const float*>(v_tile);
 #pragma unroll
     for (int kk = 0; kk < Step<BF16, D>::KK; ++kk)
-      st.k[kk] = *reinterpret_cast<const float4*>(kt + ((4 * kk + quad) * BS + 16 * h + row) * 4);
+    {
+      const float4* p = reinterpret_cast<const float4*>(kt + ((4 * kk + quad) * BS + 16 * h + row) * 4);
+      st.k[kk] = kKnt ? load_nt<float4, f32x4v>(p) : *p;
+    }
 #pragma unroll
-    for (int nt = 0; nt < Step<BF16, D>::NT; ++nt)
-      st.v[nt] = *reinterpret_cast<const float4*>(vt + (16 * nt + row) * BS + 16 * h + 4 * quad);
+    for (int nt = 0; nt < Step<BF16, D>::NT; ++nt) {
+      const float4* p = reinterpret_cast<const float4*>(vt + (16 * nt + row) * BS + 16 * h + 4 * quad);
+      st.v[nt] = kVnt ? load_nt<float4, f32x4v>(p) : *p;
+    }
   }
 }
 
@@ -359,7 +394,7 @@ __device__ __forceinline__ void merge_waves(const DecodeArgs& a, DecodeSmem<BF16
 // writes the appended token's K/V into it; the workgroup barrier after the
 // staging of the block ids orders those stores before every wave's loads
 // of the block (one workgroup: one compute unit and its L1).
-template <bool BF16, int D, int BS>
+template <bool BF16, int D, int BS, bool SH>
 __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0, int lb1, int prow, bool append,
                                DecodeSmem<BF16, D>& sm) {
   constexpr int NT = D / 16;
@@ -572,7 +607,7 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
     int u = c0 * HALVES + w;
     if (u < uend) {
       tile_ptrs(u / HALVES - c0, kt, vt);
-      load_step<BF16, D, BS>(st, kt, vt, h, row, quad);
+      load_step<BF16, D, BS, SH>(st, kt, vt, h, row, quad);
       // Every loop trip issues the next unit's loads unconditionally, so the
       // wait before the current unit's math covers only its own loads; the
       // last unit runs after the loop.
@@ -580,7 +615,7 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
         const int un = u + kWaves;
         if (un >= uend) break;
         tile_ptrs(un / HALVES - c0, kt, vt);
-        load_step<BF16, D, BS>(nxt, kt, vt, h, row, quad);
+        load_step<BF16, D, BS, SH>(nxt, kt, vt, h, row, quad);
         compute_step(st, start + 16 * u);
         st = nxt;
         u = un;
@@ -632,7 +667,7 @@ __device__ void decode_segment(const DecodeArgs& a, int s, int g, int L, int lb0
 //     fp32 FMAs, dims 16 nt + row of all GV heads over its four tokens; the
 //     quads' partial sums are added at the end of the segment.
 // GV (4 or 8) is the compile-time head count the loops run over.
-template <int D, int BS, int GV>
+template <int D, int BS, int GV, bool SH>
 __device__ void decode_segment_valu(const DecodeArgs& a, int s, int g, int L, int lb0, int lb1, int prow,
                                     bool append, DecodeSmem<true, D>& sm) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -782,12 +817,12 @@ __device__ void decode_segment_valu(const DecodeArgs& a, int s, int g, int L, in
     int u = c0 * HALVES + w;
     if (u < uend) {
       tile_ptrs(u / HALVES - c0, kt, vt);
-      load_step<true, D, BS>(st, kt, vt, h, row, quad);
+      load_step<true, D, BS, SH>(st, kt, vt, h, row, quad);
       for (;;) {
         const int un = u + kWaves;
         if (un >= uend) break;
         tile_ptrs(un / HALVES - c0, kt, vt);
-        load_step<true, D, BS>(nxt, kt, vt, h, row, quad);
+        load_step<true, D, BS, SH>(nxt, kt, vt, h, row, quad);
         compute_step(st, start + 16 * u);
         st = nxt;
         u = un;
@@ -849,19 +884,22 @@ __device__ void decode_segment_valu(const DecodeArgs& a, int s, int g, int L, in
 template <bool BF16>
 constexpr int kDecodeMinWaves = BF16 ? (PKV_DECODE_VALU_DOT ? 2 : 3) : 1;
 
-template <bool BF16, int D, int BS>
+template <bool BF16, int D, int BS, bool SH>
 __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<BF16, D> sm;
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
   // Workgroup b = k * Hkv + g serves piece k of kv head g.  The hardware
-  // deals consecutive workgroup ids round robin to the 8 XCDs; at block size
-  // 16 the ids are dealt so that each XCD runs a contiguous run of b, i.e.
-  // every head's pieces (c3 0.3802 vs 0.3833 ms, c2 0.1204 vs 0.1225 ms per
-  // step against one head per XCD); at block size 32 one head per XCD
-  // measured 1 % faster and is kept.
+  // deals consecutive workgroup ids round robin to the 8 XCDs, so with 8 kv
+  // heads each XCD serves one head.  With shared blocks that is kept: a
+  // head's shared blocks are then fetched into one L2 and found there by
+  // its other sequences (400 forked samples: 285 against 542 us with the
+  // heads spread).  Without sharing, at block size 16, the ids are dealt so
+  // that each XCD runs a contiguous run of b, i.e. every head's pieces
+  // (0.6-1 % faster on the 32k layer and the 8B-shaped batch); at block
+  // size 32 one head per XCD measured 1 % faster and is kept.
   const int n_wg = static_cast<int>(gridDim.x);
-  const int b = (BS == 16 && n_wg % 8 == 0)
+  const int b = (!SH && BS == 16 && n_wg % 8 == 0)
                     ? static_cast<int>(blockIdx.x % 8) * (n_wg / 8) + static_cast<int>(blockIdx.x / 8)
                     : static_cast<int>(blockIdx.x);
   const int g = b % Hkv;
@@ -967,12 +1005,12 @@ __global__ __launch_bounds__(kThreads, kDecodeMinWaves<BF16>) void decode_kernel
 #if PKV_DECODE_VALU_DOT
     if constexpr (BF16) {
       if (a.group <= 4)
-        decode_segment_valu<D, BS, 4>(a, s, g, L, lb0, lb1, prow, app, sm);
+        decode_segment_valu<D, BS, 4, SH>(a, s, g, L, lb0, lb1, prow, app, sm);
       else
-        decode_segment_valu<D, BS, 8>(a, s, g, L, lb0, lb1, prow, app, sm);
+        decode_segment_valu<D, BS, 8, SH>(a, s, g, L, lb0, lb1, prow, app, sm);
     } else
 #endif
-      decode_segment<BF16, D, BS>(a, s, g, L, lb0, lb1, prow, app, sm);
+      decode_segment<BF16, D, BS, SH>(a, s, g, L, lb0, lb1, prow, app, sm);
     if (lb0 == 0 && threadIdx.x == 0) {
       // Workgroup (within this head) whose range holds list position x: the
       // largest k' with k' C / Ng <= x.
@@ -1304,9 +1342,15 @@ int decode_occupancy() {
   static std::atomic<int> occ{0};
   int v = occ.load(std::memory_order_relaxed);
   if (v > 0) return v;
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<BF16, D, BS>, kThreads, 0) != hipSuccess || n <= 0)
-    n = 1;
+  // the smaller of the two cache-policy variants' (equal in practice), so
+  // the grid and the workspace size do not depend on the call's flags
+  int n0 = 0, n1 = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n0, decode_kernel<BF16, D, BS, false>, kThreads, 0) != hipSuccess)
+    n0 = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n1, decode_kernel<BF16, D, BS, true>, kThreads, 0) != hipSuccess)
+    n1 = 0;
+  int n = n0 < n1 ? n0 : n1;
+  if (n <= 0) n = 1;
   occ.store(n, std::memory_order_relaxed);
   return n;
 }
@@ -1321,18 +1365,21 @@ int occupancy_for(pkv_dtype dt, int32_t head_dim, int32_t block_size) {
 }
 
 template <bool BF16, int D, int BS>
-void launch_decode(const DecodeArgs& a, hipStream_t st) {
+void launch_decode(const DecodeArgs& a, bool shared, hipStream_t st) {
   const uint32_t nwg = static_cast<uint32_t>(static_cast<int64_t>(a.wgs_per_head) * a.num_kv_heads);
-  decode_kernel<BF16, D, BS><<<dim3(nwg), kThreads, 0, st>>>(a);
+  if (shared)
+    decode_kernel<BF16, D, BS, true><<<dim3(nwg), kThreads, 0, st>>>(a);
+  else
+    decode_kernel<BF16, D, BS, false><<<dim3(nwg), kThreads, 0, st>>>(a);
   decode_merge_kernel<BF16, D><<<dim3(a.num_kv_heads, a.num_seqs), kThreads, 0, st>>>(a);
 }
 
 template <bool BF16, int D>
-void dispatch_bs(const DecodeArgs& a, int32_t bs, hipStream_t st) {
+void dispatch_bs(const DecodeArgs& a, int32_t bs, bool shared, hipStream_t st) {
   if (bs == 16)
-    launch_decode<BF16, D, 16>(a, st);
+    launch_decode<BF16, D, 16>(a, shared, st);
   else
-    launch_decode<BF16, D, 32>(a, st);
+    launch_decode<BF16, D, 32>(a, shared, st);
 }
 
 }  // namespace
@@ -1528,9 +1575,12 @@ int32_t decode_call(void* out, const void* q, const void* k_new, const void* v_n
                     const void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
-                    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dt, void* stream,
-                    const char* what) {
+                    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dt, uint32_t flags,
+                    void* stream, const char* what) {
   if (int32_t e = check_common(head_dim, block_size, dt)) return e;
+  if (flags & ~static_cast<uint32_t>(PKV_DECODE_SHARED_BLOCKS))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "unknown decode flags 0x%x", flags);
+  const bool shared = (flags & PKV_DECODE_SHARED_BLOCKS) != 0;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0)
     return pkv::fail(PKV_ERR_INVALID_ARG,
@@ -1625,14 +1675,14 @@ int32_t decode_call(void* out, const void* q, const void* k_new, const void* v_n
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dt == PKV_BF16) {
     if (head_dim == 128)
-      dispatch_bs<true, 128>(a, block_size, st);
+      dispatch_bs<true, 128>(a, block_size, shared, st);
     else
-      dispatch_bs<true, 64>(a, block_size, st);
+      dispatch_bs<true, 64>(a, block_size, shared, st);
   } else {
     if (head_dim == 128)
-      dispatch_bs<false, 128>(a, block_size, st);
+      dispatch_bs<false, 128>(a, block_size, shared, st);
     else
-      dispatch_bs<false, 64>(a, block_size, st);
+      dispatch_bs<false, 64>(a, block_size, shared, st);
   }
   return launch_status(what);
 }
@@ -1677,10 +1727,10 @@ int32_t paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                                int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dt,
-                               void* stream) {
+                               uint32_t flags, void* stream) {
   return decode_call(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
-                     partition_size, workspace, workspace_bytes, dt, stream, "paged_attention_decode");
+                     partition_size, workspace, workspace_bytes, dt, flags, stream, "paged_attention_decode");
 }
 
 int32_t paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
@@ -1688,11 +1738,11 @@ int32_t paged_attention_decode_append(void* out, const void* q, const void* k_ne
                                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                                       int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
-                                      size_t workspace_bytes, pkv_dtype dt, void* stream) {
+                                      size_t workspace_bytes, pkv_dtype dt, uint32_t flags, void* stream) {
   if (num_seqs > 0 && (!k_new || !v_new)) return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
   return decode_call(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
-                     partition_size, workspace, workspace_bytes, dt, stream, "paged_attention_decode_append");
+                     partition_size, workspace, workspace_bytes, dt, flags, stream, "paged_attention_decode_append");
 }
 
 int32_t paged_attention_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
@@ -1700,19 +1750,20 @@ int32_t paged_attention_decode_append_noalloc(void* out, const void* q, const vo
                                               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                               int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
-                                              float scale, int32_t partition_size, pkv_dtype dt, void* stream) {
+                                              float scale, int32_t partition_size, pkv_dtype dt, uint32_t flags,
+                                              void* stream) {
   if (num_seqs > 0 && (!k_new || !v_new)) return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
   if (num_seqs <= 0)  // validation only; nothing to launch
     return decode_call(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
-                       partition_size, nullptr, 0, dt, stream, "paged_attention_decode_append_noalloc");
+                       partition_size, nullptr, 0, dt, flags, stream, "paged_attention_decode_append_noalloc");
   void* ws = nullptr;
   if (int32_t e = scratch_ptr(&ws)) return e;
   // decode_call rejects a request whose workspace exceeds the scratch with
   // PKV_ERR_CAPACITY before launching anything.
   const int32_t st = decode_call(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs,
                                  num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                                 max_context_len, scale, partition_size, ws, kScratchBytes, dt, stream,
+                                 max_context_len, scale, partition_size, ws, kScratchBytes, dt, flags, stream,
                                  "paged_attention_decode_append_noalloc");
   if (st == PKV_ERR_CAPACITY)
     pkv::fail(PKV_ERR_CAPACITY, "paged_attention_decode_append_noalloc: %s (the built-in scratch holds %zu bytes)",

@@ -19,6 +19,8 @@ def assert_same_state(native, model, sids):
     assert native.num_free() == model.num_free()
     assert native.free_stack() == model.free_stack()
     assert [native.refcount(b) for b in range(model.num_blocks)] == model.refcount
+    # the running count of blocks held more than once (the shared-blocks hint)
+    assert native.num_shared() == sum(1 for r in model.refcount if r >= 2)
     assert native.num_seqs() == len(model.tables)
     if sids:
         width = max(1, max(len(model.tables[s]) for s in sids))

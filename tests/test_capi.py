@@ -22,7 +22,7 @@ def test_header_declares_the_hot_path():
     for must in ("paged_kv_append", "paged_kv_copy_blocks", "paged_attention_decode", "pkv_bm_create",
                  "pkv_bm_append_slots", "pkv_bm_fork", "pkv_bm_free_seq", "pkv_bm_block_tables"):
         assert must in names
-    assert len(names) == 48
+    assert len(names) == 49
 
 
 def test_library_exports_every_declared_symbol():
@@ -73,8 +73,9 @@ def test_host_validation_rejects_before_any_device_call():
     dec = N.lib.paged_attention_decode
     args = [null] * 6
 
-    def call(S=2, Hq=8, Hkv=2, d=128, bs=16, nb=10, mb=4, ml=64, scale=0.1, P=0, ws=null, wsb=0, dt=N.PKV_BF16):
-        return dec(*args, S, Hq, Hkv, d, bs, nb, mb, ml, scale, P, ws, wsb, dt, null)
+    def call(S=2, Hq=8, Hkv=2, d=128, bs=16, nb=10, mb=4, ml=64, scale=0.1, P=0, ws=null, wsb=0, dt=N.PKV_BF16,
+             flags=0):
+        return dec(*args, S, Hq, Hkv, d, bs, nb, mb, ml, scale, P, ws, wsb, dt, flags, null)
 
     assert call(Hq=9) == N.PKV_ERR_INVALID_ARG  # not a multiple of Hkv
     assert call(Hq=32, Hkv=2) == N.PKV_ERR_UNSUPPORTED  # G = 16 > 8 for bf16
@@ -83,6 +84,9 @@ def test_host_validation_rejects_before_any_device_call():
     assert call(scale=float("nan")) == N.PKV_ERR_INVALID_ARG
     assert call(S=0) == 0
     assert call() == N.PKV_ERR_INVALID_ARG  # null pointers
+    assert call(S=0, flags=N.PKV_DECODE_SHARED_BLOCKS) == 0
+    assert call(S=0, flags=2) == N.PKV_ERR_INVALID_ARG  # unknown flag bit
+    assert "flags" in N.last_error()
 
 
 def test_decode_append_host_validation():
@@ -91,9 +95,9 @@ def test_decode_append_host_validation():
     null = C.c_void_p(0)
     fake = C.c_void_p(256)  # aligned, never dereferenced: every call below fails validation first
 
-    def call(kn=fake, vn=fake, S=2, Hq=8, Hkv=2, d=128, bs=16, dt=N.PKV_BF16, others=fake):
+    def call(kn=fake, vn=fake, S=2, Hq=8, Hkv=2, d=128, bs=16, dt=N.PKV_BF16, others=fake, flags=0):
         return N.lib.paged_attention_decode_append(others, others, kn, vn, others, others, others, others, S, Hq, Hkv,
-                                                   d, bs, 10, 4, 64, 0.1, 0, others, 1 << 20, dt, null)
+                                                   d, bs, 10, 4, 64, 0.1, 0, others, 1 << 20, dt, flags, null)
 
     assert call(S=0, kn=null, vn=null, others=null) == 0
     assert call(kn=null) == N.PKV_ERR_INVALID_ARG
@@ -103,6 +107,7 @@ def test_decode_append_host_validation():
     assert call(Hq=32) == N.PKV_ERR_UNSUPPORTED  # G = 16 > 8 for bf16
     assert call(d=96) == N.PKV_ERR_UNSUPPORTED
     assert call(others=null) == N.PKV_ERR_INVALID_ARG
+    assert call(flags=0x80) == N.PKV_ERR_INVALID_ARG
 
 
 def test_prefill_host_validation():

@@ -86,3 +86,46 @@ def test_stage_step_with_token_ids_registers_like_the_model():
     assert cache.bm.num_cached() == run.bm.num_cached()
     for b in range(w.num_blocks):
         assert cache.bm.cached_digest(b) == run.bm.block_digest[b]
+
+
+@pytest.mark.parametrize("name,over", [
+    ("c6_prefix_cache_bf16", SMALL),
+    ("c4_prefix_bf16", dict(prefix_len=300, num_prompts=4, n_samples=4, suffix_max=40, num_blocks=400)),
+    ("c2_8b_bf16", dict(lengths=[300, 17, 1, 64, 129, 2000], num_blocks=400)),
+])
+def test_shared_blocks_flag_changes_only_the_schedule(name, over):
+    """The decode calls' cache-policy flag (PKV_DECODE_SHARED_BLOCKS: cached
+    loads, one kv head per XCD; else non-temporal streaming loads and, at
+    block size 16, every head on every XCD) gives bit-identical outputs, on
+    a batch whose sequences share prompt blocks and on one whose blocks are
+    all private; both equal the oracle."""
+    import paged_kv_cache_230_amd as pkv
+
+    w = Workload(name, overrides=over)
+    cache = product_cache(w)
+    run = OracleRun(w)
+    kn, vn = w.kv(("step", 0))
+    cache.append(w.decode_seqs, [1] * w.num_seqs, kn, vn, token_ids=w.step_tokens(0))
+    run.step(0)
+    shared = cache.bm.num_shared()
+    say(f"case {name}: {w.num_seqs} sequences, {shared} shared blocks")
+    if name != "c2_8b_bf16":
+        assert shared > 0
+    else:
+        assert shared == 0
+    q = w.q(0).to(cache.device)
+    tables, lens, _, lh = cache.tables(w.decode_seqs)
+    outs = {}
+    for flag in (False, True):
+        for part in (0, 64):
+            out = torch.full_like(q, float("nan"))
+            pkv.device_status()
+            pkv.paged_attention_decode(out, q, cache.k_cache, cache.v_cache, tables, lens, int(lh.max()),
+                                       partition_size=part, shared_blocks=flag)
+            assert pkv.device_status() == 0
+            outs[(flag, part)] = out
+    torch.cuda.synchronize()
+    for part in (0, 64):
+        assert torch.equal(outs[(False, part)].view(torch.int16), outs[(True, part)].view(torch.int16)), \
+            f"{name} partition {part}: outputs differ between the cache policies"
+        assert_close(outs[(True, part)], run.attention(w.q(0)), "bf16", f"{name} partition {part} vs oracle")

@@ -61,11 +61,13 @@ def test_no_vector_register_spills_and_design_occupancy(tmp_path):
     for name, u in found.items():
         assert "vgpr_spill" in u and "waves" in u, f"incomplete remarks for {name}"
         assert u["vgpr_spill"] == 0, f"{name} spills {u['vgpr_spill']} vector registers"
-    # bf16 decode at head_dim 128 (the 8B/70B-shaped layers): three waves per SIMD
+    # bf16 decode at head_dim 128 (the 8B/70B-shaped layers), both cache
+    # policies (streamed, shared blocks): three waves per SIMD
     for bs in (16, 32):
-        key = f"_ZN12_GLOBAL__N_113decode_kernelILb1ELi128ELi{bs}EEEvNS_10DecodeArgsE"
-        assert key in found, f"missing {key}"
-        assert found[key]["waves"] >= 3, f"{key}: {found[key]['waves']} waves per SIMD"
+        for shared in (0, 1):
+            key = f"_ZN12_GLOBAL__N_113decode_kernelILb1ELi128ELi{bs}ELb{shared}EEEvNS_10DecodeArgsE"
+            assert key in found, f"missing {key}"
+            assert found[key]["waves"] >= 3, f"{key}: {found[key]['waves']} waves per SIMD"
     # chunked prefill at head_dim 128: two waves per SIMD (8 waves, one workgroup per compute unit)
     for bs in (16, 32):
         key = f"_ZN12_GLOBAL__N_114prefill_kernelILi128ELi{bs}EEEvNS_11PrefillArgsE"
