@@ -92,6 +92,8 @@ def test_stage_step_with_token_ids_registers_like_the_model():
     ("c6_prefix_cache_bf16", SMALL),
     ("c4_prefix_bf16", dict(prefix_len=300, num_prompts=4, n_samples=4, suffix_max=40, num_blocks=400)),
     ("c2_8b_bf16", dict(lengths=[300, 17, 1, 64, 129, 2000], num_blocks=400)),
+    ("c5_mixed_bs32_bf16", dict(lengths=[16, 40, 33, 100, 1000, 64, 65, 31, 2], num_blocks=80)),
+    ("c1_tiny_f32", {}),
 ])
 def test_shared_blocks_flag_changes_only_the_schedule(name, over):
     """The decode calls' cache-policy flag (PKV_DECODE_SHARED_BLOCKS: cached
@@ -109,10 +111,11 @@ def test_shared_blocks_flag_changes_only_the_schedule(name, over):
     run.step(0)
     shared = cache.bm.num_shared()
     say(f"case {name}: {w.num_seqs} sequences, {shared} shared blocks")
-    if name != "c2_8b_bf16":
+    if name in ("c6_prefix_cache_bf16", "c4_prefix_bf16"):
         assert shared > 0
     else:
         assert shared == 0
+    kind = "f32" if w.config.dtype == "f32" else "bf16"
     q = w.q(0).to(cache.device)
     tables, lens, _, lh = cache.tables(w.decode_seqs)
     outs = {}
@@ -126,6 +129,7 @@ def test_shared_blocks_flag_changes_only_the_schedule(name, over):
             outs[(flag, part)] = out
     torch.cuda.synchronize()
     for part in (0, 64):
-        assert torch.equal(outs[(False, part)].view(torch.int16), outs[(True, part)].view(torch.int16)), \
-            f"{name} partition {part}: outputs differ between the cache policies"
-        assert_close(outs[(True, part)], run.attention(w.q(0)), "bf16", f"{name} partition {part} vs oracle")
+        a, b = outs[(False, part)], outs[(True, part)]
+        bits = torch.int32 if a.dtype == torch.float32 else torch.int16
+        assert torch.equal(a.view(bits), b.view(bits)), f"{name} partition {part}: outputs differ between the cache policies"
+        assert_close(b, run.attention(w.q(0)), kind, f"{name} partition {part} vs oracle")
