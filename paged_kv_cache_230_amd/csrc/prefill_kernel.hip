@@ -50,6 +50,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float float16v;
 // A 16-byte chunk as a plain vector type.
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
@@ -494,14 +496,20 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     // the bf16 rounding of the remainder, so it is carried to about 2^-17
     // relative precision (one bf16 alone, 2^-9, leaves outputs near zero
     // with relative errors of tens of percent).
-    __bf16 pe[16], pr[16];
+    // Converted in pairs: one packed conversion gives two high parts, whose
+    // fp32 values are the packed word shifted or masked; one more gives the
+    // two low parts.
+    uint32_t pe2[8], pr2[8];
     float sum;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(x[j], a.scale_log2, -m_use));
-      sum = j ? sum + p : p;
-      pe[j] = static_cast<__bf16>(p);
-      pr[j] = static_cast<__bf16>(p - static_cast<float>(pe[j]));
+    for (int j2 = 0; j2 < 8; ++j2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * j2], a.scale_log2, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * j2 + 1], a.scale_log2, -m_use));
+      sum = j2 ? sum + p0 + p1 : p0 + p1;
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+      const float h0 = __builtin_bit_cast(float, hi << 16), h1 = __builtin_bit_cast(float, hi & 0xFFFF0000u);
+      pe2[j2] = hi;
+      pr2[j2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0 - h0, p1 - h1}, bf16x2));
     }
     l_run = l_run * alpha + sum;
 
@@ -514,10 +522,8 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     const char* sl = reinterpret_cast<const char*>(sm.stage[cur]);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const bf16x8 pb = bf16x8{pe[8 * m], pe[8 * m + 1], pe[8 * m + 2], pe[8 * m + 3],
-                               pe[8 * m + 4], pe[8 * m + 5], pe[8 * m + 6], pe[8 * m + 7]};
-      const bf16x8 pbl = bf16x8{pr[8 * m], pr[8 * m + 1], pr[8 * m + 2], pr[8 * m + 3],
-                                pr[8 * m + 4], pr[8 * m + 5], pr[8 * m + 6], pr[8 * m + 7]};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pe2[4 * m], pe2[4 * m + 1], pe2[4 * m + 2], pe2[4 * m + 3]});
+      const bf16x8 pbl = __builtin_bit_cast(bf16x8, u32x4{pr2[4 * m], pr2[4 * m + 1], pr2[4 * m + 2], pr2[4 * m + 3]});
 #pragma unroll
       for (int t = 0; t < kDimTiles; ++t) {
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(sl + v_off[m] + t * 32 * (BS / 8) * 16);
