@@ -159,6 +159,30 @@ def measured_read_peak(dev, nbytes=4 << 30, reps=6):
     return rates[-1], rates[len(rates) // 2]
 
 
+def measured_mfma_peak(dev, workgroups=2048, iters=4096, reps=5):
+    """bf16 matrix-core rate of the library's probe (pkv_mfma_rate: every
+    wave issues 32x32x16 products into independent register accumulators),
+    timed with HIP events on the current stream: (best, median) in flop/s
+    over ``reps`` runs of about 20 ms after one untimed run.  The GPU lowers
+    its clock under this load, so the rate sits below the nominal peak."""
+    import torch
+
+    import paged_kv_cache_230_amd as pkv
+
+    sink = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
+    pkv.mfma_rate(sink, workgroups, iters)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    flops = 0
+    for r in range(reps):
+        flops = pkv.mfma_rate(sink, workgroups, iters)
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    rates = sorted(flops / (ev[r].elapsed_time(ev[r + 1]) / 1e3) for r in range(reps))
+    del sink
+    return rates[-1], rates[len(rates) // 2]
+
+
 def percentiles(xs, ps=(10, 50, 90)):
     """Nearest-rank percentiles of a list."""
     ys = sorted(xs)
@@ -328,6 +352,7 @@ def run_prefill(args, w, dev):
     flops = [prefill_flops(step_lens[k], w.chunk_lens, c.num_q_heads, c.head_dim) for k in timed]
     achieved = sum(flops) / sum(call_s)
     value = sum(flops) / elapsed
+    peak_mfma, median_mfma = (None, None) if args.no_read_peak else measured_mfma_peak(dev)
     return {
         "metric": PREFILL_METRIC,
         "value": round(value / 1e12, 2),
@@ -364,6 +389,11 @@ def run_prefill(args, w, dev):
             "traffic": load_prefill_traffic(w.name, args.steps, args.warmup),
             "traffic_unit": "HBM bytes per call, mean over the timed calls",
             "algorithmic_flops_per_call_mean": int(sum(flops) / len(flops)),
+            # the probe's issued bf16 matrix-core rate; the kernel issues 1.5
+            # products per useful one (the probabilities' low parts)
+            "measured_mfma_peak_tflops": round(peak_mfma / 1e12, 1) if peak_mfma else None,
+            "measured_mfma_median_tflops": round(median_mfma / 1e12, 1) if median_mfma else None,
+            "frac_of_measured_peak": round(achieved / peak_mfma, 4) if peak_mfma else None,
         },
         "cpu_baseline": None,
     }
@@ -739,7 +769,8 @@ def main():
                          "paged_attention_decode_append")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences in the oracle sample (default: all)")
     ap.add_argument("--no-read-peak", action="store_true",
-                    help="skip the streaming-read probe (for counter runs, which would count its reads too)")
+                    help="skip the ceiling probes: streaming read (decode), matrix-core rate (prefill); for counter "
+                         "and trace runs, which would count their work too")
     ap.add_argument("--overlap-stage", action="store_true",
                     help="stage step k+1's bookkeeping on a second stream during step k's decode (two buffer sets)")
     ap.add_argument("--marked", type=int, default=50,

@@ -114,6 +114,21 @@ const char* pkv_last_error(void);
  * Asynchronous on `stream`. */
 int32_t pkv_stream_read(const void* buf, size_t bytes, void* sink, int32_t sink_words, void* stream);
 
+/* Measurement helper: launches `workgroups` workgroups of 512 threads (8
+ * waves); every wave issues `iters` x 16 bf16 matrix products
+ * v_mfma_f32_32x32x16_bf16 (32768 flops each) on register operands into four
+ * independent accumulators, and every thread writes one float to
+ * sink[workgroup * 512 + thread] (device float [workgroups * 512], 4-byte
+ * aligned, owned by the caller).  Flops issued: workgroups * 8 * iters * 16 *
+ * 32768.  Timing it gives the bf16 matrix-core rate this GPU sustains (it
+ * lowers its clock under such load), the practical ceiling beside the
+ * nominal peak for the matrix-core-bound chunked prefill ([aitalk] the
+ * part on the two independent problems: prefill computes the prompt's K/V
+ * and attention).  Errors: null or misaligned sink, workgroups <= 0,
+ * iters < 0 (PKV_ERR_INVALID_ARG), launch failure (PKV_ERR_DEVICE).
+ * Asynchronous on `stream`. */
+int32_t pkv_mfma_rate(void* sink, int32_t workgroups, int32_t iters, void* stream);
+
 /* Library interface version (major * 100 + minor). */
 int32_t pkv_version(void);
 

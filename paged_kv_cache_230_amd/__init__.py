@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     block_digest,
     device_status,
     stream_read,
+    mfma_rate,
     host_pools,
     new_pools,
     paged_attention_decode,

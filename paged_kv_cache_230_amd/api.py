@@ -89,6 +89,20 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor):
                                   _stream(dev)))
 
 
+def mfma_rate(sink: torch.Tensor, workgroups: int, iters: int) -> int:
+    """Run the library's matrix-core probe on the current stream:
+    ``workgroups`` workgroups of 8 waves, each wave issuing ``iters`` x 16
+    bf16 32x32x16 products; ``sink`` (device float32, at least
+    ``workgroups * 512`` elements) receives one value per thread.  Returns
+    the flops issued."""
+    dev = sink.device
+    _need(sink, "sink", torch.float32, dev, 1)
+    if sink.numel() < workgroups * 512:
+        raise ValueError(f"sink holds {sink.numel()} floats, needs {workgroups * 512}")
+    N.check(N.lib.pkv_mfma_rate(_ptr(sink), workgroups, iters, _stream(dev)))
+    return workgroups * 8 * iters * 16 * 32768
+
+
 def pool_shapes(num_blocks, num_kv_heads, head_dim, block_size, dtype):
     x = 16 // torch.empty((), dtype=dtype).element_size()
     return ((num_blocks, num_kv_heads, head_dim // x, block_size, x), (num_blocks, num_kv_heads, head_dim, block_size))

@@ -1,9 +1,12 @@
-// Measurement helper: the HBM read rate a plain streaming kernel reaches on
-// this GPU, the practical ceiling a bandwidth-bound kernel is compared with
-// beside the nominal peak.  The paged decode kernel is bound by HBM
-// bandwidth ("PagedAttention" (robocikowo.com), Złożoność obliczeniowa), so
-// its achieved rate is reported against both.
+// Measurement helpers: the rates plain probe kernels reach on this GPU, the
+// practical ceilings the hot kernels are compared with beside the nominal
+// peaks.  The paged decode kernel is bound by HBM bandwidth ("PagedAttention"
+// (robocikowo.com), Złożoność obliczeniowa); the chunked prefill, which
+// computes the prompt's attention once per chunk ("PagedAttention et
+// RadixAttention : parlons de KV Cache", the part on the two independent
+// problems), by the matrix cores.
 //
+// Streaming read:
 // Each workgroup reads one contiguous share of the buffer; each lane reads
 // 16-byte chunks (a wave a contiguous 1 KiB run) with kUnroll independent
 // loads in flight before any is used.  (Contiguous shares measured 3-5 %
@@ -13,6 +16,12 @@
 // way measured 6.2 TB/s against 7.0 TB/s.  The loaded words are folded by
 // XOR into one word per workgroup, written to `sink`, so no load can be
 // dropped.
+//
+// Matrix-core rate: every wave issues v_mfma_f32_32x32x16_bf16 (the prefill
+// kernel's product) into four independent accumulators, operands in
+// registers, no memory traffic but one store per lane at the end.  Under
+// such sustained matrix-core load the GPU lowers its clock below the
+// nominal 2.4 GHz, so this rate is below the published dense peak.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -54,9 +63,50 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
   }
 }
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float float16v;
+constexpr int kMfmaThreads = 512;  // 8 waves: 2 per SIMD
+constexpr int kMfmaPerIter = 16;   // products per wave and iteration
+
+__global__ __launch_bounds__(kMfmaThreads) void mfma_rate_kernel(float* __restrict__ sink, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(static_cast<float>((lane + i) & 15) * 0.0625f);
+    b[i] = static_cast<__bf16>(static_cast<float>((lane ^ i) & 7) * 0.125f);
+  }
+  float16v c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < kMfmaPerIter / 4; ++k) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc += c0[i] + c1[i] + c2[i] + c3[i];
+  sink[static_cast<int64_t>(blockIdx.x) * kMfmaThreads + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t pkv_mfma_rate(void* sink, int32_t workgroups, int32_t iters, void* stream) {
+  if (!sink) return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (workgroups <= 0 || iters < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "workgroups %d must be > 0 and iters %d >= 0", workgroups, iters);
+  if ((reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return pkv::fail(PKV_ERR_INVALID_ARG, "sink must be 4-byte aligned");
+  mfma_rate_kernel<<<dim3(static_cast<uint32_t>(workgroups)), kMfmaThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<float*>(sink), iters);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::fail(PKV_ERR_DEVICE, "pkv_mfma_rate launch failed: %s", hipGetErrorString(e));
+  return pkv::ok();
+}
 
 int32_t pkv_stream_read(const void* buf, size_t bytes, void* sink, int32_t sink_words, void* stream) {
   if (!buf || !sink) return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");

@@ -21,7 +21,7 @@
 //     ahead, as permutations of the pool's 16-byte chunks (layouts at
 //     StageLayout); V slots past the context are zeroed in LDS, so unused
 //     slots of the last block never reach the products.  A workgroup
-//     barrier closes every third step only, so the waves need not run in
+//     barrier closes every second step only, so the waves need not run in
 //     lockstep.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the step's 32 keys (in slot
 //     order) in the rows, the wave's 32 query rows in the columns.  Lane l
@@ -31,6 +31,12 @@
 //   * The probabilities enter the value product as bf16 high and low parts
 //     (two products per tile), so they keep about 2^-17 relative precision;
 //     the scores are two chained half dot products summed at the end.
+//   * The value product of a step is issued one step after its scores, so
+//     each step holds two independent parts: the matrix-core products (the
+//     previous step's value product, the next step's scores) and the
+//     softmax on the vector ALUs.  The two waves sharing a SIMD run the
+//     parts in opposite orders, so that one issues products while the other
+//     computes exponentials.
 //   * Online softmax per row in the log2 domain; row maxima by the gfx950
 //     row swap v_permlane32_swap, not LDS shuffles; the causal mask (a
 //     select, never a multiply) only on the steps that reach past the tile's
@@ -41,6 +47,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "pkv_status.h"
 
@@ -117,16 +124,17 @@ struct StageLayout {
   static_assert((kStageBytes / 16) % kPThreads == 0, "stage must split evenly over the threads");
 };
 
-// Stage ring: during step st the PV product reads stage st, the QK product
+// Stage ring: during step st the PV product reads stage st - 1, the QK product
 // of step st + 1 reads stage st + 1, and the loads of step st + kAhead are
-// issued into the stage step st - kBarrierEvery used (all modulo kStages);
-// the stages in between are landing.
+// issued into the stage step st - kBarrierEvery - 1 used (all modulo
+// kStages); the stages in between are landing.
 constexpr int kStages = 8;
 // A workgroup barrier closes every kBarrierEvery-th step; between barriers
-// the waves may run up to that many steps apart, so a stage may be reloaded
-// only that many steps after its last reader.
-constexpr int kBarrierEvery = 3;
-constexpr int kAhead = kStages - kBarrierEvery;
+// the waves may run up to kBarrierEvery - 1 steps apart, and a stage's last
+// reader is the value product one step after its scores, so a stage may be
+// reloaded only kBarrierEvery + 1 steps after its scores were computed.
+constexpr int kBarrierEvery = 2;
+constexpr int kAhead = kStages - kBarrierEvery - 1;
 static_assert(kAhead >= kBarrierEvery + 1, "the stage read next must have landed at each barrier");
 template <int D>
 struct PrefillSmem {
@@ -405,10 +413,6 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   // stages 0 .. kBarrierEvery landed; later steps up to min(kAhead, nsteps) - 1 may be in flight
   constexpr int kInFlight = kAhead - kBarrierEvery - 1;  // steps a barrier lets stay in flight
   barrier_after_steps<kPer, kInFlight>((nsteps < kAhead ? nsteps : kAhead) - kBarrierEvery - 1);
-  if (nsteps == 1 && tail) {
-    zero_v_tail<D, BS>(sm.stage[0], 0, L);
-    stage_barrier<0>();
-  }
 
   const int key_col = lane & 31;  // QK A operand slot of this lane
   const int k_tile = key_col / BS, k_in = key_col % BS;
@@ -440,8 +444,52 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   }
   static_assert(32 % (8 / (BS / 8)) == 0, "the V swizzle repeats within 32 dims");
 
-  auto step = [&](int st, int cur, const float16v& sc, float16v& sn) __attribute__((always_inline)) {
-    const int nx1 = (cur + 1) % kStages, nxa = (cur + kAhead) % kStages;
+  // Probabilities of the step whose value product is issued next, as bf16
+  // pairs: high parts and the bf16 roundings of the remainders (keys
+  // 16(j/8) + 8*half + j%8 for j = 2*i, 2*i + 1).
+  uint32_t pe2[8], pr2[8];
+  // The rescale of the accumulators that the previous step's row max asks
+  // for; it is applied just before that step's value product.
+  float alpha_prev = 1.f;
+  bool move_prev = false;
+
+  // O^T += V^T P^T for the step whose scores gave pe2/pr2, from the V part
+  // of its stage: two products of 16 keys; product m takes this lane's
+  // scores j = 8m..8m+7, keys 16m + 8*half + i, the B operand's k order; the
+  // V operand of lane l holds the same keys of dim 32t + l%32.  The high and
+  // low parts of P each take one product with the same V operand.
+  auto pv = [&](const char* sl, const uint32_t (&pe)[8], const uint32_t (&pr)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pe[4 * m], pe[4 * m + 1], pe[4 * m + 2], pe[4 * m + 3]});
+      const bf16x8 pbl = __builtin_bit_cast(bf16x8, u32x4{pr[4 * m], pr[4 * m + 1], pr[4 * m + 2], pr[4 * m + 3]});
+      // All high-part products, then all low-part ones: a product that adds
+      // to an accumulator then trails the previous one on it by kDimTiles
+      // issues, not one (+1.5 %).
+      bf16x8 va[kDimTiles];
+#pragma unroll
+      for (int t = 0; t < kDimTiles; ++t) va[t] = *reinterpret_cast<const bf16x8*>(sl + v_off[m] + t * 32 * (BS / 8) * 16);
+#pragma unroll
+      for (int t = 0; t < kDimTiles; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb, acc[t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < kDimTiles; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pbl, acc[t], 0, 0, 0);
+    }
+  };
+  auto rescale_prev = [&]() __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(move_prev)) {  // rare
+#pragma unroll
+      for (int t = 0; t < kDimTiles; ++t) acc[t] *= alpha_prev;
+    }
+  };
+
+  // Step st: scores of step st (sc) -> probabilities; scores of step st + 1
+  // (sn); the value product of step st - 1.  The value product trails its
+  // scores by a step so that one basic block holds both products and the
+  // softmax of the step, which share no operands: the wave's matrix-core
+  // and vector-ALU work can then overlap.
+  auto step = [&](auto with_pv, auto mfma_first, int st, int cur, const float16v& sc, float16v& sn)
+                  __attribute__((always_inline)) {
+    const int nx1 = (cur + 1) % kStages, nxa = (cur + kAhead) % kStages, prv = (cur + kStages - 1) % kStages;
     if (st + kAhead < nsteps) {
       load_stage<D, BS>(sm.stage[nxa], plan, stride, ids);
       if (st + kAhead + 1 < nsteps) {
@@ -454,82 +502,85 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         ids.read(sm.ids, (st + kAhead + 1) * kTiles - chunk_base);  // its loads are issued a step later
       }
     }
-    const bool zero = tail && st + 1 == nsteps - 1;  // stage st + 1 landed at the last barrier
-    if (zero) zero_v_tail<D, BS>(sm.stage[nx1], (st + 1) * kKeys, L);
 
-    // The softmax part of the step (row max, rescale, the next step's QK
-    // issue, the exponentials) runs at raised wave priority and the value
-    // products at the normal one, so of the two waves on a SIMD the one
-    // working through its vector-ALU chain is issued first while the other's
-    // matrix-core products run (+2-4 % against no priority change, and 3 %
-    // better than raising it for the products instead).  Block size 16
-    // only: at 32 the instantiation then spills two registers.
-    if constexpr (BS == 16) __builtin_amdgcn_s_setprio(1);
-    // ---- row max of step st (raw scores; the scale is positive, so it
-    // commutes with the max and is folded into the exponent below).
-    float x[16];  // raw scores of keys 16(j/8) + 8*half + j%8
+    // Raw scores of keys 16(j/8) + 8*half + j%8, masked past the row's
+    // position (a select, never a multiply).  The branches come before the
+    // products so that they do not split the products off the softmax.
+    float x[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) x[j] = sc[j];
     if (st >= mask_from) {
+      const int lim = row_pos - st * kKeys - 8 * half;
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (st * kKeys + 16 * (j / 8) + 8 * half + (j % 8) > row_pos) x[j] = -INFINITY;
+        if (16 * (j / 8) + (j % 8) > lim) x[j] = -INFINITY;
     }
-    float mx = fmaxf(x[0], x[1]);
-#pragma unroll
-    for (int j = 2; j < 16; ++j) mx = fmaxf(mx, x[j]);
-    mx = reduce_pair<true>(mx) * a.scale_log2;
-    const bool move = mx > m_run + kSlack;
-    const float m_use = move ? mx : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_use;
-    if (__builtin_amdgcn_ballot_w64(move)) {  // rare: before the products so they share one basic block
-#pragma unroll
-      for (int t = 0; t < kDimTiles; ++t) acc[t] *= alpha;
-    }
+    if constexpr (decltype(with_pv)::value) rescale_prev();
 
-    // ---- scores of step st + 1 (on the last step this reads a stage whose
-    // contents are unused: in bounds, result dropped).
-    sn = qk(reinterpret_cast<const char*>(sm.stage[nx1]));
-
-    // Each probability enters the value product as a bf16 high part and
-    // the bf16 rounding of the remainder, so it is carried to about 2^-17
-    // relative precision (one bf16 alone, 2^-9, leaves outputs near zero
-    // with relative errors of tens of percent).
-    // Converted in pairs: one packed conversion gives two high parts, whose
-    // fp32 values are the packed word shifted or masked; one more gives the
-    // two low parts.
-    uint32_t pe2[8], pr2[8];
-    float sum;
+    uint32_t pe_prev[8], pr_prev[8];  // the probabilities of step st - 1
 #pragma unroll
     for (int j2 = 0; j2 < 8; ++j2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * j2], a.scale_log2, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * j2 + 1], a.scale_log2, -m_use));
-      sum = j2 ? sum + p0 + p1 : p0 + p1;
-      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
-      const float h0 = __builtin_bit_cast(float, hi << 16), h1 = __builtin_bit_cast(float, hi & 0xFFFF0000u);
-      pe2[j2] = hi;
-      pr2[j2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0 - h0, p1 - h1}, bf16x2));
+      pe_prev[j2] = pe2[j2];
+      pr_prev[j2] = pr2[j2];
     }
-    l_run = l_run * alpha + sum;
-
-    // ---- O^T += V^T P^T, two products of 16 keys: product m takes this
-    // lane's scores j = 8m..8m+7, keys 16m + 8*half + i, the B operand's k
-    // order; the V operand of lane l holds the same keys of dim 32t + l%32.
-    // The high and low parts of P each take one product with the same V
-    // operand.
-    if constexpr (BS == 16) __builtin_amdgcn_s_setprio(0);
-    const char* sl = reinterpret_cast<const char*>(sm.stage[cur]);
+    // The matrix-core products of the step: the value product of step
+    // st - 1 and the scores of step st + 1 (on the last step this reads a
+    // stage whose contents are unused: in bounds, result dropped).
+    auto products = [&]() __attribute__((always_inline)) {
+      if constexpr (decltype(with_pv)::value) pv(reinterpret_cast<const char*>(sm.stage[prv]), pe_prev, pr_prev);
+      sn = qk(reinterpret_cast<const char*>(sm.stage[nx1]));
+    };
+    // The vector-ALU part: the softmax of step st.
+    auto softmax = [&]() __attribute__((always_inline)) {
+      // ---- row max (raw scores; the scale is positive, so it commutes
+      // with the max and is folded into the exponent below).
+      float mx = fmaxf(x[0], x[1]);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pe2[4 * m], pe2[4 * m + 1], pe2[4 * m + 2], pe2[4 * m + 3]});
-      const bf16x8 pbl = __builtin_bit_cast(bf16x8, u32x4{pr2[4 * m], pr2[4 * m + 1], pr2[4 * m + 2], pr2[4 * m + 3]});
+      for (int j = 2; j < 16; ++j) mx = fmaxf(mx, x[j]);
+      mx = reduce_pair<true>(mx) * a.scale_log2;
+      const bool move = mx > m_run + kSlack;
+      const float m_use = move ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_use;
+      // Each probability enters the value product as a bf16 high part and
+      // the bf16 rounding of the remainder, so it is carried to about 2^-17
+      // relative precision (one bf16 alone, 2^-9, leaves outputs near zero
+      // with relative errors of tens of percent).
+      // Converted in pairs: one packed conversion gives two high parts,
+      // whose fp32 values are the packed word shifted or masked; one more
+      // gives the two low parts.
+      float sum;
 #pragma unroll
-      for (int t = 0; t < kDimTiles; ++t) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(sl + v_off[m] + t * 32 * (BS / 8) * 16);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbl, acc[t], 0, 0, 0);
+      for (int j2 = 0; j2 < 8; ++j2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * j2], a.scale_log2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * j2 + 1], a.scale_log2, -m_use));
+        sum = j2 ? sum + p0 + p1 : p0 + p1;
+        const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+        const float h0 = __builtin_bit_cast(float, hi << 16), h1 = __builtin_bit_cast(float, hi & 0xFFFF0000u);
+        pe2[j2] = hi;
+        pr2[j2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0 - h0, p1 - h1}, bf16x2));
       }
+      // Keep the probabilities in this step: the compiler would otherwise
+      // sink their computation into the next step, next to their only use.
+#pragma unroll
+      for (int j2 = 0; j2 < 8; ++j2) asm volatile("" : "+v"(pe2[j2]), "+v"(pr2[j2]));
+      l_run = l_run * alpha + sum;
+      alpha_prev = alpha;
+      move_prev = move;
+    };
+    // The two waves sharing a SIMD (waves w and w + 4) take the two parts in
+    // opposite orders, so that after each barrier one issues matrix-core
+    // products while the other runs its softmax on the vector ALUs.  The
+    // scheduling barrier keeps the instruction scheduler from interleaving
+    // the parts within a wave (+1 % against one order for all waves).
+    if constexpr (decltype(mfma_first)::value) {
+      products();
+      __builtin_amdgcn_sched_barrier(0);
+      softmax();
+    } else {
+      softmax();
+      __builtin_amdgcn_sched_barrier(0);
+      products();
     }
 
     // The barrier closing step st (every kBarrierEvery-th step) leaves
@@ -538,19 +589,38 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     // min(st + kAhead, nsteps - 1) may be in flight.
     if ((st + 1) % kBarrierEvery == 0)
       barrier_after_steps<kPer, kInFlight>((nsteps - 1 - st < kAhead ? nsteps - 1 - st : kAhead) - kBarrierEvery - 1);
-    else if (zero)
-      stage_barrier<63>();  // publish the zeroed slots before PV(st + 1)
   };
 
-  float16v s0 = qk(reinterpret_cast<const char*>(sm.stage[0])), s1;
-  int st = 0, cur = 0;
-  for (; st + 1 < nsteps; st += 2) {  // unrolled by two: the score sets swap roles
-    step(st, cur, s0, s1);
-    cur = (cur + 1) % kStages;
-    step(st + 1, cur, s1, s0);
-    cur = (cur + 1) % kStages;
+  using no_pv = std::integral_constant<bool, false>;
+  using with_pv = std::integral_constant<bool, true>;
+  auto run_steps = [&](auto mfma_first) __attribute__((always_inline)) {
+    float16v s0 = qk(reinterpret_cast<const char*>(sm.stage[0])), s1;
+    step(no_pv{}, mfma_first, 0, 0, s0, s1);
+    int st = 1, cur = 1;
+    for (; st + 1 < nsteps; st += 2) {  // unrolled by two: the score sets swap roles
+      step(with_pv{}, mfma_first, st, cur, s1, s0);
+      cur = (cur + 1) % kStages;
+      step(with_pv{}, mfma_first, st + 1, cur, s0, s1);
+      cur = (cur + 1) % kStages;
+    }
+    if (st < nsteps) {
+      step(with_pv{}, mfma_first, st, cur, s1, s0);
+      cur = (cur + 1) % kStages;
+    }
+    return cur;
+  };
+  const int cur = (wave & 4) ? run_steps(std::integral_constant<bool, false>{})
+                             : run_steps(std::integral_constant<bool, true>{});
+  // ---- the last step's value product; if the context ends inside that
+  // step, its V slots past the end are zeroed first (no wave reads that
+  // stage's V part before this point, and no load is in flight into it).
+  const int last = (cur + kStages - 1) % kStages;
+  if (tail) {
+    zero_v_tail<D, BS>(sm.stage[last], (nsteps - 1) * kKeys, L);
+    stage_barrier<63>();
   }
-  if (st < nsteps) step(st, cur, s0, s1);
+  rescale_prev();
+  pv(reinterpret_cast<const char*>(sm.stage[last]), pe2, pr2);
 
   // ---- normalise and store: lane holds dims 32t + 8(j/4) + 4*half + j%4 of its row.
   const float l = reduce_pair<false>(l_run);
