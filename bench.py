@@ -159,6 +159,42 @@ def measured_read_peak(dev, nbytes=4 << 30, reps=6):
     return rates[-1], rates[len(rates) // 2]
 
 
+def measured_tile_read(dev, cache, tables, lens, block_size, reps=6):
+    """Rate at which the library's tile probe (pkv_tile_read) streams the
+    very (block, kv head) tiles of K and V that a decode call over
+    ``tables``/``lens`` reads, head by head and sequence by sequence, with
+    no arithmetic: (best, median) in bytes/s over ``reps`` reads after one
+    untimed read, timed with HIP events on the current stream."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_230_amd as pkv
+
+    hkv = cache.k_cache.shape[1]
+    nb = -(-np.asarray(lens, dtype=np.int64) // block_size)
+    blocks = np.concatenate([np.asarray(tables[s, :nb[s]], dtype=np.int64) for s in range(len(nb))])
+    ids = np.concatenate([blocks * hkv + g for g in range(hkv)]).astype(np.int32)
+    tile = cache.k_cache[0, 0].numel() * cache.k_cache.element_size()
+    ids_d = torch.from_numpy(ids).to(dev)
+    sink = torch.empty(16384, dtype=torch.int32, device=dev)
+
+    def read():
+        pkv.tile_read(cache.k_cache, tile, ids_d, sink)
+        pkv.tile_read(cache.v_cache, tile, ids_d, sink)
+
+    read()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for r in range(reps):
+        read()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    nbytes = 2 * ids.size * tile
+    rates = sorted(nbytes / (ev[r].elapsed_time(ev[r + 1]) / 1e3) for r in range(reps))
+    del ids_d, sink
+    return rates[-1], rates[len(rates) // 2]
+
+
 def measured_mfma_peak(dev, workgroups=2048, iters=4096, reps=5):
     """bf16 matrix-core rate of the library's probe (pkv_mfma_rate: every
     wave issues 32x32x16 products into independent register accumulators),
@@ -769,8 +805,8 @@ def main():
                          "paged_attention_decode_append")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences in the oracle sample (default: all)")
     ap.add_argument("--no-read-peak", action="store_true",
-                    help="skip the ceiling probes: streaming read (decode), matrix-core rate (prefill); for counter "
-                         "and trace runs, which would count their work too")
+                    help="skip the ceiling probes: streaming and tile reads (decode), matrix-core rate (prefill); for "
+                         "counter and trace runs, which would count their work too")
     ap.add_argument("--overlap-stage", action="store_true",
                     help="stage step k+1's bookkeeping on a second stream during step k's decode (two buffer sets)")
     ap.add_argument("--marked", type=int, default=50,
@@ -996,6 +1032,8 @@ def main():
     step_gbps = [b / (t * 1e-6) / 1e9 for b, t in zip(step_kv, step_us)]
     dec_us = [1e3 * t for t in dec_ms]
     peak_read, median_read = (None, None) if args.no_read_peak else measured_read_peak(dev)
+    tile_read, tile_median = ((None, None) if args.no_read_peak
+                              else measured_tile_read(dev, cache, t_host, l_host, bs))
     ms_per_step = elapsed / args.steps * 1e3
     value = sum(kv_bytes) / elapsed / 1e9
     traffic = load_traffic(w.name, P) if not args.separate_append else None
@@ -1056,6 +1094,10 @@ def main():
             "measured_read_peak_gbps": round(peak_read / 1e9, 1) if peak_read else None,
             "measured_read_median_gbps": round(median_read / 1e9, 1) if median_read else None,
             "frac_of_measured_peak": round(achieved / peak_read, 4) if peak_read else None,
+            # the same call's K/V tiles streamed by pkv_tile_read, no arithmetic
+            "measured_tile_read_gbps": round(tile_read / 1e9, 1) if tile_read else None,
+            "measured_tile_read_median_gbps": round(tile_median / 1e9, 1) if tile_median else None,
+            "frac_of_tile_read": round(achieved / tile_read, 4) if tile_read else None,
         },
         "step_distribution": {
             "steps": len(step_us),

@@ -114,6 +114,23 @@ const char* pkv_last_error(void);
  * Asynchronous on `stream`. */
 int32_t pkv_stream_read(const void* buf, size_t bytes, void* sink, int32_t sink_words, void* stream);
 
+/* Measurement helper: reads num_tiles tiles of tile_bytes (a positive
+ * multiple of 1024) at base + ids[i] * tile_bytes once each, with the same
+ * non-temporal 16-byte loads as pkv_stream_read; ids (device int32
+ * [num_tiles]) are clamped to [0, max_tiles), so every read stays inside
+ * base's max_tiles tiles (base 16-byte aligned).  Each wave reads whole
+ * tiles of a contiguous share of the list; at most sink_words workgroups,
+ * each folding what it read into one word of `sink` (device uint32
+ * [sink_words]).  Run over the (block, kv head) tiles a decode call reads,
+ * it gives the rate at which those very tiles can be streamed without any
+ * arithmetic: the ceiling of the bandwidth-bound decode kernel for that
+ * access pattern ([pl] Złożoność obliczeniowa; [aitalk] step 2: the blocks
+ * are scattered through the pool).  Errors: null pointers, misalignment,
+ * bad sizes (PKV_ERR_INVALID_ARG), launch failure (PKV_ERR_DEVICE).
+ * Asynchronous on `stream`. */
+int32_t pkv_tile_read(const void* base, size_t tile_bytes, size_t max_tiles, const int32_t* ids, int64_t num_tiles,
+                      void* sink, int32_t sink_words, void* stream);
+
 /* Measurement helper: launches `workgroups` workgroups of 512 threads (8
  * waves); every wave issues `iters` x 16 bf16 matrix products
  * v_mfma_f32_32x32x16_bf16 (32768 flops each) on register operands into four

@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     device_status,
     stream_read,
     mfma_rate,
+    tile_read,
     host_pools,
     new_pools,
     paged_attention_decode,

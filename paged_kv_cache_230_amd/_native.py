@@ -76,6 +76,7 @@ _SIGS = {
     "pkv_device_status": (_i32, [_vp, _i32, _pi32]),
     "pkv_stream_read": (_i32, [_vp, _sz, _vp, _i32, _vp]),
     "pkv_mfma_rate": (_i32, [_vp, _i32, _i32, _vp]),
+    "pkv_tile_read": (_i32, [_vp, _sz, _sz, _vp, _i64, _vp, _i32, _vp]),
     "paged_kv_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "paged_kv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "paged_attention_decode": (

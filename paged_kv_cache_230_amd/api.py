@@ -89,6 +89,23 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor):
                                   _stream(dev)))
 
 
+def tile_read(pool: torch.Tensor, tile_bytes: int, ids: torch.Tensor, sink: torch.Tensor):
+    """Read the tiles ``pool`` + ids[i] * tile_bytes (``pool`` a contiguous
+    device tensor; ``ids`` device int32, clamped to the pool's tiles) once
+    with the library's tile probe on the current stream; ``sink`` (device
+    int32) receives one word per workgroup."""
+    dev = pool.device
+    _need(ids, "ids", torch.int32, dev, 1)
+    _need(sink, "sink", torch.int32, dev, 1)
+    if not pool.is_contiguous():
+        raise ValueError("pool must be contiguous")
+    nbytes = pool.numel() * pool.element_size()
+    if tile_bytes <= 0 or nbytes < tile_bytes:
+        raise ValueError(f"tile_bytes {tile_bytes} does not fit a pool of {nbytes} bytes")
+    N.check(N.lib.pkv_tile_read(_ptr(pool), tile_bytes, nbytes // tile_bytes, _ptr(ids), ids.numel(), _ptr(sink),
+                                sink.numel(), _stream(dev)))
+
+
 def mfma_rate(sink: torch.Tensor, workgroups: int, iters: int) -> int:
     """Run the library's matrix-core probe on the current stream:
     ``workgroups`` workgroups of 8 waves, each wave issuing ``iters`` x 16

@@ -17,6 +17,12 @@
 // XOR into one word per workgroup, written to `sink`, so no load can be
 // dropped.
 //
+// Tile read: the same loads over a list of fixed-size tiles at given indices
+// (the decode kernel reads each (block, kv head) tile of K and V, 4 KiB at
+// 70B shape, at scattered places of the pool).  Each wave reads whole tiles
+// of a contiguous share of the list, 1 KiB per load instruction, two tiles
+// in flight.  Indices are clamped to the pool, so every read stays inside it.
+//
 // Matrix-core rate: every wave issues v_mfma_f32_32x32x16_bf16 (the prefill
 // kernel's product) into four independent accumulators, operands in
 // registers, no memory traffic but one store per lane at the end.  Under
@@ -63,6 +69,57 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
   }
 }
 
+constexpr int kTileUnroll = 2;
+
+__global__ __launch_bounds__(kThreads) void tile_read_kernel(const char* __restrict__ base, int64_t tile_bytes,
+                                                             const int32_t* __restrict__ ids, int64_t num_tiles,
+                                                             int64_t max_tiles, uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  const int64_t t0 = num_tiles * wave / nwaves, t1 = num_tiles * (wave + 1) / nwaves;
+  const int64_t runs = tile_bytes / 1024;  // 1 KiB per wave-wide load
+  auto tile_at = [&](int64_t t) {
+    int64_t id = ids[t];
+    id = id < 0 ? 0 : (id >= max_tiles ? max_tiles - 1 : id);
+    return reinterpret_cast<const u32x4v*>(base + id * tile_bytes);
+  };
+  uint32_t acc = 0;
+  int64_t t = t0;
+  for (; t + kTileUnroll <= t1; t += kTileUnroll) {
+    const u32x4v* tp[kTileUnroll];
+#pragma unroll
+    for (int u = 0; u < kTileUnroll; ++u) tp[u] = tile_at(t + u);
+    for (int64_t r = 0; r < runs; r += 4) {
+      u32x4v v[kTileUnroll][4];
+#pragma unroll
+      for (int u = 0; u < kTileUnroll; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[u][q] = r + q < runs ? __builtin_nontemporal_load(tp[u] + (r + q) * 64 + lane) : u32x4v{};
+#pragma unroll
+      for (int u = 0; u < kTileUnroll; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc ^= v[u][q].x ^ v[u][q].y ^ v[u][q].z ^ v[u][q].w;
+    }
+  }
+  for (; t < t1; ++t) {
+    const u32x4v* tp = tile_at(t);
+    for (int64_t r = 0; r < runs; ++r) {
+      const u32x4v v = __builtin_nontemporal_load(tp + r * 64 + lane);
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  __shared__ uint32_t wv[kThreads / 64];
+  if (lane == 0) wv[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t x = 0;
+    for (int w = 0; w < kThreads / 64; ++w) x ^= wv[w];
+    sink[blockIdx.x] = x;
+  }
+}
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float float16v;
 constexpr int kMfmaThreads = 512;  // 8 waves: 2 per SIMD
@@ -95,6 +152,28 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_rate_kernel(float* __restri
 }  // namespace
 
 extern "C" {
+
+int32_t pkv_tile_read(const void* base, size_t tile_bytes, size_t max_tiles, const int32_t* ids, int64_t num_tiles,
+                      void* sink, int32_t sink_words, void* stream) {
+  if (!base || !sink || (num_tiles > 0 && !ids)) return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if ((reinterpret_cast<uintptr_t>(base) & 15u) != 0 || tile_bytes == 0 || tile_bytes % 1024 != 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "base must be 16-byte aligned and tile_bytes a positive multiple of 1024");
+  if (max_tiles == 0 || max_tiles > static_cast<size_t>(INT64_MAX) / tile_bytes)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "max_tiles %zu out of range", max_tiles);
+  if (num_tiles < 0 || sink_words <= 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_tiles %lld < 0 or sink_words %d <= 0", static_cast<long long>(num_tiles),
+                     sink_words);
+  if (num_tiles == 0) return pkv::ok();
+  const int64_t waves = (num_tiles + kTileUnroll - 1) / kTileUnroll;
+  int64_t grid = (waves + kThreads / 64 - 1) / (kThreads / 64);
+  if (grid > sink_words) grid = sink_words;
+  tile_read_kernel<<<dim3(static_cast<uint32_t>(grid)), kThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const char*>(base), static_cast<int64_t>(tile_bytes), ids, num_tiles, static_cast<int64_t>(max_tiles),
+      static_cast<uint32_t*>(sink));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::fail(PKV_ERR_DEVICE, "pkv_tile_read launch failed: %s", hipGetErrorString(e));
+  return pkv::ok();
+}
 
 int32_t pkv_mfma_rate(void* sink, int32_t workgroups, int32_t iters, void* stream) {
   if (!sink) return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");

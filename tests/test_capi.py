@@ -22,7 +22,7 @@ def test_header_declares_the_hot_path():
     for must in ("paged_kv_append", "paged_kv_copy_blocks", "paged_attention_decode", "pkv_bm_create",
                  "pkv_bm_append_slots", "pkv_bm_fork", "pkv_bm_free_seq", "pkv_bm_block_tables"):
         assert must in names
-    assert len(names) == 50
+    assert len(names) == 51
 
 
 def test_library_exports_every_declared_symbol():
@@ -59,6 +59,20 @@ def test_mfma_probe_validates_arguments():
     assert N.lib.pkv_mfma_rate(C.c_void_p(256), 4, -1, None) == N.PKV_ERR_INVALID_ARG
     assert N.lib.pkv_mfma_rate(C.c_void_p(258), 4, 1, None) == N.PKV_ERR_INVALID_ARG
     assert "aligned" in N.last_error()
+
+
+def test_tile_probe_validates_arguments():
+    import paged_kv_cache_230_amd._native as N
+
+    ids = C.c_void_p(256)
+    assert N.lib.pkv_tile_read(C.c_void_p(0), 4096, 8, ids, 4, C.c_void_p(256), 16, None) == N.PKV_ERR_INVALID_ARG
+    assert "null" in N.last_error()
+    assert N.lib.pkv_tile_read(C.c_void_p(256), 1000, 8, ids, 4, C.c_void_p(256), 16, None) == N.PKV_ERR_INVALID_ARG
+    assert N.lib.pkv_tile_read(C.c_void_p(264), 4096, 8, ids, 4, C.c_void_p(256), 16, None) == N.PKV_ERR_INVALID_ARG
+    assert N.lib.pkv_tile_read(C.c_void_p(256), 4096, 0, ids, 4, C.c_void_p(256), 16, None) == N.PKV_ERR_INVALID_ARG
+    assert N.lib.pkv_tile_read(C.c_void_p(256), 4096, 8, ids, -1, C.c_void_p(256), 16, None) == N.PKV_ERR_INVALID_ARG
+    assert N.lib.pkv_tile_read(C.c_void_p(256), 4096, 8, ids, 4, C.c_void_p(256), 0, None) == N.PKV_ERR_INVALID_ARG
+    assert N.lib.pkv_tile_read(C.c_void_p(256), 4096, 8, ids, 0, C.c_void_p(256), 16, None) == N.PKV_OK
 
 
 def test_device_status_rejects_null_output():
