@@ -141,8 +141,9 @@ int32_t pkv_tile_read(const void* base, size_t tile_bytes, size_t max_tiles, con
  * lowers its clock under such load), the practical ceiling beside the
  * nominal peak for the matrix-core-bound chunked prefill ([aitalk] the
  * part on the two independent problems: prefill computes the prompt's K/V
- * and attention).  Errors: null or misaligned sink, workgroups <= 0,
- * iters < 0 (PKV_ERR_INVALID_ARG), launch failure (PKV_ERR_DEVICE).
+ * and attention).  Errors: null or misaligned sink, workgroups <= 0 or
+ * above 8388607 (2^32 - 1 work-items), iters < 0 (PKV_ERR_INVALID_ARG),
+ * launch failure (PKV_ERR_DEVICE).
  * Asynchronous on `stream`. */
 int32_t pkv_mfma_rate(void* sink, int32_t workgroups, int32_t iters, void* stream);
 

@@ -179,6 +179,9 @@ int32_t pkv_mfma_rate(void* sink, int32_t workgroups, int32_t iters, void* strea
   if (!sink) return pkv::fail(PKV_ERR_INVALID_ARG, "null pointer argument");
   if (workgroups <= 0 || iters < 0)
     return pkv::fail(PKV_ERR_INVALID_ARG, "workgroups %d must be > 0 and iters %d >= 0", workgroups, iters);
+  if (static_cast<int64_t>(workgroups) > static_cast<int64_t>(UINT32_MAX / kMfmaThreads))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "workgroups %d exceeds the %u a launch holds", workgroups,
+                     static_cast<unsigned>(UINT32_MAX / kMfmaThreads));
   if ((reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return pkv::fail(PKV_ERR_INVALID_ARG, "sink must be 4-byte aligned");
   mfma_rate_kernel<<<dim3(static_cast<uint32_t>(workgroups)), kMfmaThreads, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<float*>(sink), iters);

@@ -57,6 +57,7 @@ def test_mfma_probe_validates_arguments():
     assert "null" in N.last_error()
     assert N.lib.pkv_mfma_rate(C.c_void_p(256), 0, 1, None) == N.PKV_ERR_INVALID_ARG
     assert N.lib.pkv_mfma_rate(C.c_void_p(256), 4, -1, None) == N.PKV_ERR_INVALID_ARG
+    assert N.lib.pkv_mfma_rate(C.c_void_p(256), 8388608, 1, None) == N.PKV_ERR_INVALID_ARG
     assert N.lib.pkv_mfma_rate(C.c_void_p(258), 4, 1, None) == N.PKV_ERR_INVALID_ARG
     assert "aligned" in N.last_error()
 
