@@ -159,21 +159,31 @@ def measured_read_peak(dev, nbytes=4 << 30, reps=6):
     return rates[-1], rates[len(rates) // 2]
 
 
+def decode_tile_ids(tables, lens, block_size, num_kv_heads):
+    """The (block, kv head) tiles a decode call reads, as tile indices
+    block * num_kv_heads + head into a pool laid out [block][kv head][tile],
+    in the kernel's visiting order: head by head, each head's sequences in
+    order, each sequence's blocks in logical order.  Empty sequences read
+    nothing."""
+    import numpy as np
+
+    nb = -(-np.asarray(lens, dtype=np.int64) // block_size)
+    parts = [np.asarray(tables[s, :nb[s]], dtype=np.int64) for s in range(len(nb))]
+    blocks = np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+    return np.concatenate([blocks * num_kv_heads + g for g in range(num_kv_heads)]).astype(np.int32)
+
+
 def measured_tile_read(dev, cache, tables, lens, block_size, reps=6):
     """Rate at which the library's tile probe (pkv_tile_read) streams the
     very (block, kv head) tiles of K and V that a decode call over
     ``tables``/``lens`` reads, head by head and sequence by sequence, with
     no arithmetic: (best, median) in bytes/s over ``reps`` reads after one
     untimed read, timed with HIP events on the current stream."""
-    import numpy as np
     import torch
 
     import paged_kv_cache_230_amd as pkv
 
-    hkv = cache.k_cache.shape[1]
-    nb = -(-np.asarray(lens, dtype=np.int64) // block_size)
-    blocks = np.concatenate([np.asarray(tables[s, :nb[s]], dtype=np.int64) for s in range(len(nb))])
-    ids = np.concatenate([blocks * hkv + g for g in range(hkv)]).astype(np.int32)
+    ids = decode_tile_ids(tables, lens, block_size, cache.k_cache.shape[1])
     tile = cache.k_cache[0, 0].numel() * cache.k_cache.element_size()
     ids_d = torch.from_numpy(ids).to(dev)
     sink = torch.empty(16384, dtype=torch.int32, device=dev)

@@ -55,3 +55,25 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120, cwd=root)
     assert r.returncode == 2
     assert "exactly one GPU" in r.stderr and r.stdout == ""
+
+
+def test_decode_tile_ids_are_the_tiles_a_decode_call_reads():
+    """The tile-read ceiling streams exactly the (block, kv head) tiles of the
+    call: every block of each sequence's first ceil(L / bs) table entries,
+    for every kv head, head by head; empty sequences add nothing."""
+    import numpy as np
+
+    rng = np.random.default_rng(5)
+    bs, hkv, width = 16, 4, 9
+    lens = np.array([1, 0, 16, 17, 140, 33], dtype=np.int32)
+    tables = rng.permutation(200)[: len(lens) * width].reshape(len(lens), width).astype(np.int32)
+    ids = bench.decode_tile_ids(tables, lens, bs, hkv)
+    nb = [-(-int(L) // bs) for L in lens]
+    per_head = sum(nb)
+    assert ids.dtype == np.int32 and ids.size == hkv * per_head
+    rows = np.concatenate([tables[s, :nb[s]] for s in range(len(lens))])
+    for g in range(hkv):
+        seg = ids[g * per_head:(g + 1) * per_head].astype(np.int64)
+        assert np.array_equal(seg % hkv, np.full(per_head, g))
+        assert np.array_equal(seg // hkv, rows)
+    assert bench.decode_tile_ids(tables[:2], np.array([0, 0]), bs, hkv).size == 0
